@@ -1,0 +1,197 @@
+"""Benchmark of one GPT-2 pretraining step (forward + loss, backward, AdamW) on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload gpt2_124m] [--no-cpu]
+
+A step is the whole hot path over one micro-batch of seeded synthetic tokens already resident in
+HBM: gpt2_forward_loss + gpt2_backward + gpt2_adamw_step. value = tokens per second over the K
+timed steps. MFU counts 6N + 6 L T d FLOPs per token ("Pré-treinar um LLM", paragraphs on the
+6ND derivation and on Kaplan's Eq. (2.2), with N counting the embeddings) against the MI355X
+dense bf16 peak. One JSON line is printed on stdout.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PAGES_TOKENS_PER_S = 120_000.0  # GPT-2 124M on one RTX 4090 (context only)
+HBM_PEAK_GBS = 8000.0
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "lm_head_gemm_traffic.json")
+
+
+def _source_hash() -> str:
+    h = hashlib.sha256()
+    for f in ("gemm.hip", "common.h", "kernels.h"):
+        with open(os.path.join(ROOT, "transformer_lm_pretraining_gpt_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def _traffic(workload: str):
+    """HBM bytes per LM-head GEMM launch from the committed rocprofv3 counter summary, or None
+    when it is absent or was taken on another version of the GEMM source."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            t = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if t.get("source_hash") != _source_hash() or t.get("workload") != workload:
+        return None
+    return t.get("bytes_per_launch")
+
+
+def cpu_baseline(model, ocfg, x, y):
+    """The float64 oracle, untuned, on one sequence of the bench batch: forward, backward and
+    AdamW for the full model at seq_len T. Returns the cpu_baseline object."""
+    import numpy as np
+
+    import oracle as O
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max((i.get("num_threads", 1) for i in threadpool_info()), default=1)
+    except Exception:
+        threads = len(os.sched_getaffinity(0))
+    p = model.params()
+    one = O.Config(ocfg.n_layer, ocfg.d_model, ocfg.n_head, ocfg.seq_len, ocfg.vocab,
+                   ocfg.vocab_padded, 1)
+    m = np.zeros(p.size)
+    v = np.zeros(p.size)
+    t0 = time.perf_counter()
+    O.step(p, m, v, 1, x[:1], y[:1], one)
+    dt = time.perf_counter() - t0
+    return {"value": round(ocfg.seq_len / dt, 2), "unit": "tokens/s", "cores": threads,
+            "kind": "oracle",
+            "sample": f"one full step (float64 forward, backward, AdamW over all {p.size} "
+                      f"parameters) on 1 of the {ocfg.batch} sequences ({ocfg.seq_len} tokens) of "
+                      f"the bench batch; {dt:.1f} s"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="gpt2_124m")
+    ap.add_argument("--no-cpu", action="store_true", help="skip the oracle's cpu_baseline leg")
+    ap.add_argument("--no-breakdown", action="store_true", help="skip per-family kernel timing")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(json.dumps({"error": "this build runs on exactly one GPU; --gpus must be 1",
+                          "n_gpus": args.gpus}))
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import oracle as O
+    from transformer_lm_pretraining_gpt_amd import PEAK_BF16_FLOPS, PRESETS, flops_per_token
+    from transformer_lm_pretraining_gpt_amd import gpt2 as G
+    from transformer_lm_pretraining_gpt_amd import synthetic as S
+
+    L, d, H, T, V, Vp, B, prec, kind = PRESETS[args.workload]
+    cfg = G.Config.make(L, d, H, T, V, Vp, B, prec, seed=1234)
+    ocfg = O.Config(L, d, H, T, V, Vp, B)
+    M = B * T
+    torch.cuda.set_device(0)
+    model = G.GPT2(cfg)
+    nwin = args.warmup + args.steps
+    stream = S.tokens_for(kind, B, T, V, seed=1234, windows=nwin)
+    xs, ys = [], []
+    for i in range(nwin):
+        x, y = S.batch_from_stream(stream, B, T, i)
+        xs.append(torch.from_numpy(x).cuda())
+        ys.append(torch.from_numpy(y).cuda())
+    loss = torch.zeros(1, dtype=torch.float32, device="cuda")
+
+    def step(i):
+        model.forward_loss(xs[i], ys[i], loss)
+        model.backward(1.0, False)
+        model.adamw_step(6e-4, 0.9, 0.95, 1e-8, 0.1)
+
+    for i in range(args.warmup):
+        step(i)
+    model.check()
+    torch.cuda.synchronize()
+
+    # ---- timed region: K whole steps; the LM-head GEMM is bracketed by HIP events live ----
+    model.timing_begin("lm_head_gemm")
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    ev0.record()
+    t0 = time.perf_counter()
+    for i in range(args.warmup, nwin):
+        step(i)
+    ev1.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms_total = ev0.elapsed_time(ev1)
+    lm_ms, lm_n, lm_work = model.timing_end()
+    model.check()
+    final_loss = float(loss.item())
+
+    ms_per_step = ms_total / args.steps
+    tok_s = M * args.steps / (ms_total / 1e3)
+    ftok = flops_per_token(L, d, Vp, T)
+    mfu = tok_s * ftok / PEAK_BF16_FLOPS
+    lm_avg_ms = lm_ms / max(lm_n, 1)
+    lm_flops = lm_work / max(lm_n, 1)
+    achieved = lm_flops / (lm_avg_ms / 1e3) / 1e12
+    peak_tf = PEAK_BF16_FLOPS / 1e12
+    roof = {"bound": "mfma", "kernel": "LM-head forward GEMM (gemm_kernel<bf16,1,1,256,256,1>)",
+            "achieved": round(achieved, 2), "peak": round(peak_tf, 1), "unit": "TFLOP/s",
+            "frac": round(achieved / peak_tf, 4), "traffic": _traffic(args.workload),
+            "flops_per_launch": lm_flops, "avg_launch_ms": round(lm_avg_ms, 4),
+            "launches_timed": lm_n}
+
+    out = {
+        "metric": "train tokens/sec + MFU (6ND+attn FLOPs) for GPT-2 124M, T=1024, 1 GPU",
+        "value": round(tok_s, 1), "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(ms_per_step, 3), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": round(tok_s / PAGES_TOKENS_PER_S, 3),
+        "baseline_context": "pages: ~120k tokens/s, GPT-2 124M, micro-batch 16x1024, one RTX 4090",
+        "mfu": round(mfu, 4), "flops_per_token": ftok, "dtype": prec,
+        "data": "synthetic: seeded Zipf(1.1) token stream over 50257 ids; random-init weights",
+        "config": {"workload": f"{args.workload}: L={L} d={d} H={H} T={T} vocab={V}->{Vp} "
+                               f"micro-batch={B}, forward+backward+AdamW per step",
+                   "tokens_per_step": M, "seq_len": T, "micro_batch": B, "parallelism": "none"},
+        "final_loss": round(final_loss, 4), "wall_s_timed": round(wall, 3),
+        "roofline": roof,
+    }
+
+    # ---- per-family kernel timing (separate passes, not part of value) ----
+    if not args.no_breakdown:
+        fams = {}
+        for fam, unit in (("gemm", "TFLOP/s"), ("attention_fwd", "TFLOP/s"), ("xent", "GB/s"),
+                          ("adamw", "GB/s")):
+            model.timing_begin(fam)
+            for i in range(args.warmup, min(nwin, args.warmup + 3)):
+                step(i)
+            ms, n, work = model.timing_end()
+            if n == 0:
+                continue
+            rate = work / (ms / 1e3)
+            if unit == "TFLOP/s":
+                fams[fam] = {"ms_per_step": round(ms / 3, 3), "launches": n,
+                             "achieved": round(rate / 1e12, 1), "unit": unit,
+                             "frac": round(rate / PEAK_BF16_FLOPS, 4)}
+            else:
+                fams[fam] = {"ms_per_step": round(ms / 3, 3), "launches": n,
+                             "achieved": round(rate / 1e9, 1), "unit": unit,
+                             "frac": round(rate / 1e9 / HBM_PEAK_GBS, 4)}
+        out["kernels"] = fams
+
+    if not args.no_cpu:
+        x0, y0 = S.batch_from_stream(stream, B, T, 0)
+        out["cpu_baseline"] = cpu_baseline(model, ocfg, x0, y0)
+    model.close()
+    print(json.dumps(out))
+
+
+if __name__ == "__main__":
+    main()

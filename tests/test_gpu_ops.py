@@ -1,0 +1,132 @@
+"""Kernel-level parity on the GPU, through the C ABI's single-kernel entry points:
+the MFMA GEMM (bitwise on small-integer bf16 inputs, whose fp32 sums are exact) and causal
+attention forward/backward against the float64 oracle."""
+import math
+
+import numpy as np
+import pytest
+
+import oracle as O
+from gpu_util import cosine, normwise_rel, torch_cuda
+from transformer_lm_pretraining_gpt_amd import gpt2 as G
+
+pytestmark = pytest.mark.gpu
+
+
+def _stored(torch, logical, kmajor_rows_are_k, dtype):
+    """Device copy of a logical (R, K) operand stored [r][k] (kmajor) or [k][r]."""
+    arr = logical if kmajor_rows_are_k else logical.T
+    return torch.from_numpy(np.ascontiguousarray(arr)).to(dtype).cuda()
+
+
+LAYOUTS = [(1, 0), (1, 1), (0, 0), (0, 1)]
+SHAPES = [(200, 136, 72), (256, 256, 128), (1000, 520, 776), (4096, 2304, 768), (64, 768, 3072)]
+
+
+@pytest.mark.parametrize("layout", LAYOUTS)
+@pytest.mark.parametrize("shape", SHAPES)
+def test_gemm_bf16_exact_integers(layout, shape):
+    torch = torch_cuda()
+    ak, bk = layout
+    m, n, k = shape
+    rng = np.random.default_rng(m * 7 + n * 3 + k + 11 * ak + 5 * bk)
+    a = rng.integers(-4, 5, size=(m, k)).astype(np.float32)
+    b = rng.integers(-4, 5, size=(k, n)).astype(np.float32)  # logical (k, n)
+    da = _stored(torch, a, ak == 1, torch.bfloat16)            # [m][k] or [k][m]
+    db = _stored(torch, b.T, bk == 1, torch.bfloat16)          # [n][k] or [k][n]
+    c = torch.full((m, n), float("nan"), dtype=torch.float32, device="cuda")
+    G.op_gemm(da, db, c, a_kmajor=ak, b_kmajor=bk, m=m, n=n, k=k, precision="bf16")
+    torch.cuda.synchronize()
+    ref = (a.astype(np.float64) @ b.astype(np.float64)).astype(np.float32)
+    assert np.array_equal(c.cpu().numpy(), ref)
+
+
+def test_gemm_bf16_lm_head_shape_exact():
+    """The LM-head product shape (vocab 50304, ragged against 256-wide tiles), integer inputs."""
+    torch = torch_cuda()
+    m, n, k = 2048, 50304, 768
+    rng = np.random.default_rng(3)
+    a = rng.integers(-3, 4, size=(m, k)).astype(np.float32)
+    w = rng.integers(-3, 4, size=(n, k)).astype(np.float32)  # stored [n][k] like the embedding
+    c = torch.empty((m, n), dtype=torch.float32, device="cuda")
+    G.op_gemm(torch.from_numpy(a).to(torch.bfloat16).cuda(),
+              torch.from_numpy(w).to(torch.bfloat16).cuda(), c, a_kmajor=1, b_kmajor=1,
+              m=m, n=n, k=k, precision="bf16")
+    torch.cuda.synchronize()
+    ref = a.astype(np.float64) @ w.T.astype(np.float64)
+    assert np.array_equal(c.cpu().numpy(), ref.astype(np.float32))
+
+
+@pytest.mark.parametrize("layout", LAYOUTS)
+def test_gemm_fp32_alpha_beta(layout):
+    torch = torch_cuda()
+    ak, bk = layout
+    m, n, k = 328, 200, 264
+    rng = np.random.default_rng(9)
+    a = rng.standard_normal((m, k)).astype(np.float32)
+    b = rng.standard_normal((k, n)).astype(np.float32)
+    c0 = rng.standard_normal((m, n)).astype(np.float32)
+    c = torch.from_numpy(c0).cuda()
+    G.op_gemm(_stored(torch, a, ak == 1, torch.float32), _stored(torch, b.T, bk == 1, torch.float32),
+              c, a_kmajor=ak, b_kmajor=bk, m=m, n=n, k=k, alpha=0.5, beta=-2.0, precision="fp32")
+    torch.cuda.synchronize()
+    ref = 0.5 * (a.astype(np.float64) @ b) - 2.0 * c0
+    assert normwise_rel(c.cpu().numpy(), ref) < 2e-6
+
+
+def _attn_case(torch, prec, B, T, H, hd, seed):
+    d = H * hd
+    rng = np.random.default_rng(seed)
+    qkv = (rng.standard_normal((B * T, 3 * d)) * 1.5).astype(np.float32)
+    dout = rng.standard_normal((B * T, d)).astype(np.float32)
+    tdt = torch.bfloat16 if prec == "bf16" else torch.float32
+    if prec == "bf16":  # the oracle sees exactly the values the kernel sees
+        qkv = torch.from_numpy(qkv).to(tdt).float().numpy()
+        dout = torch.from_numpy(dout).to(tdt).float().numpy()
+    g_qkv = torch.from_numpy(qkv).to(tdt).cuda()
+    g_out = torch.empty((B * T, d), dtype=tdt, device="cuda")
+    g_lse = torch.empty((B, H, T), dtype=torch.float32, device="cuda")
+    G.op_attention_forward(g_qkv, g_out, g_lse, B, T, H, hd, precision=prec)
+    g_dout = torch.from_numpy(dout).to(tdt).cuda()
+    g_dqkv = torch.full((B * T, 3 * d), float("nan"), dtype=tdt, device="cuda")
+    scratch = torch.empty((B * H * T,), dtype=torch.float32, device="cuda")
+    G.op_attention_backward(g_qkv, g_out, g_lse, g_dout, g_dqkv, scratch, B, T, H, hd,
+                            precision=prec)
+    torch.cuda.synchronize()
+    cfg = O.Config(1, d, H, T, 8, 8, B)
+    q, k, v = (qkv[:, i * d:(i + 1) * d].astype(np.float64) for i in range(3))
+    o = O.gpt2_oracle.attention_forward(q, k, v, cfg)
+    dq, dk, dv = O.gpt2_oracle.attention_backward(dout.astype(np.float64), q, k, v, cfg)
+    lse = np.empty((B, H, T))
+    for b in range(B):
+        for h in range(H):
+            s = q[b * T:(b + 1) * T, h * hd:(h + 1) * hd] @ k[b * T:(b + 1) * T, h * hd:(h + 1) * hd].T
+            s = s / math.sqrt(hd)
+            s[np.triu_indices(T, k=1)] = -np.inf
+            mx = s.max(axis=1)
+            lse[b, h] = mx + np.log(np.exp(s - mx[:, None]).sum(axis=1))
+    got = dict(o=g_out.float().cpu().numpy(), lse=g_lse.cpu().numpy(),
+               dqkv=g_dqkv.float().cpu().numpy())
+    return got, dict(o=o, lse=lse, dqkv=np.concatenate([dq, dk, dv], axis=1))
+
+
+@pytest.mark.parametrize("hd", [16, 32, 64])
+@pytest.mark.parametrize("T", [1, 64, 200])
+def test_attention_fp32(hd, T):
+    torch = torch_cuda()
+    got, ref = _attn_case(torch, "fp32", 2, T, 3, hd, seed=hd + T)
+    assert normwise_rel(got["lse"], ref["lse"]) < 1e-5
+    assert normwise_rel(got["o"], ref["o"]) < 1e-5
+    assert normwise_rel(got["dqkv"], ref["dqkv"]) < 1e-5
+
+
+@pytest.mark.parametrize("hd,T,H", [(64, 200, 3), (64, 1024, 2), (32, 136, 2), (16, 72, 4)])
+def test_attention_bf16(hd, T, H):
+    torch = torch_cuda()
+    got, ref = _attn_case(torch, "bf16", 2, T, H, hd, seed=3 * hd + T)
+    assert normwise_rel(got["lse"], ref["lse"]) < 1e-3
+    assert cosine(got["o"], ref["o"]) > 0.9999
+    d = H * hd
+    for i, part in enumerate(("dq", "dk", "dv")):
+        g, r = got["dqkv"][:, i * d:(i + 1) * d], ref["dqkv"][:, i * d:(i + 1) * d]
+        assert cosine(g, r) > 0.999, part

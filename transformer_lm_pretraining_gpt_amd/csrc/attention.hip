@@ -1,0 +1,484 @@
+// Causal multi-head attention, forward and backward, tiled with online softmax (gfx950 MFMA).
+//
+// Per (batch, head): O = softmax(Q K^T / sqrt(hd), keys j <= query i) V. This is the O(T^2) term
+// that Kaplan's Eq. (2.2) adds to the 2N forward cost ("Pré-treinar um LLM", paragraph on the
+// attention term). No T x T matrix ever reaches memory: scores live in MFMA accumulators.
+//
+// Orientation. The forward computes S^T = K Q^T: the 32x32 MFMA result puts one query per lane
+// (column) and 16 keys per lane in registers, so the softmax row statistics of a query are a
+// per-lane reduction plus one exchange with the other lane half, and the probabilities are
+// already laid out as the B operand of O^T = V^T P^T (no trip through LDS). V^T is staged
+// transposed in LDS so its fragments line up with the probabilities' key order.
+//
+// Backward (deterministic, no atomics): kernel 1 owns a block of keys and accumulates dK, dV
+// over all later queries (S = Q K^T orientation: one key per lane); kernel 2 owns a block of
+// queries and accumulates dQ over all earlier keys (S^T orientation). Both recompute P from the
+// saved row log-sum-exp, and use D_i = sum_d dO_id O_id, computed by a small kernel first:
+//   dV = P^T dO,  dP = dO V^T,  dS = P o (dP - D),  dQ = dS K / sqrt(hd),  dK = dS^T Q / sqrt(hd).
+#include <math.h>
+
+#include "common.h"
+#include "kernels.h"
+
+namespace {
+
+constexpr int THREADS = 256;
+constexpr int BKV = 64;  // keys (or queries) per LDS stage
+constexpr float LOG2E = 1.4426950408889634f;
+constexpr float LN2 = 0.6931471805599453f;
+
+template <typename T, int HD>
+struct AttnGeom {
+  static constexpr int VE = 16 / (int)sizeof(T);             // elements per 16-byte vector
+  static constexpr int ROWBYTES = HD * (int)sizeof(T);        // one head row
+  static constexpr int CPR = ROWBYTES / 16;                   // 16-byte chunks per head row
+  static constexpr int NS = ROWBYTES / 32;                    // MFMA k-steps over head_dim
+  static constexpr int RP = ROWBYTES + 16;                    // padded LDS pitch, row layout
+  static constexpr int TP = BKV * (int)sizeof(T) + (sizeof(T) == 2 ? 8 : 16);  // transposed
+  static constexpr int DB = HD / 32 > 0 ? HD / 32 : 1;        // 32-row blocks of head_dim
+  static_assert(HD % 32 == 0 || HD == 16, "head_dim");
+};
+
+// Stage rows [row0, row0+64) of a head (one 16-byte chunk per thread step) into row layout.
+template <typename T, int HD>
+DEV void stage_rows(char* lds, const T* base, int64_t ld, int row0, int nrows, int tid) {
+  using G = AttnGeom<T, HD>;
+  for (int c = tid; c < BKV * G::CPR; c += THREADS) {
+    const int r = c / G::CPR, ch = c % G::CPR;
+    u32x4 v{0, 0, 0, 0};
+    if (row0 + r < nrows) v = ld16(base + (int64_t)(row0 + r) * ld + ch * G::VE);
+    st16(lds + r * G::RP + ch * 16, v);
+  }
+}
+
+// Stage rows [row0, row0+64) of a head transposed: lds[d][r] (r contiguous). A task is 4 rows x
+// one 16-byte vector of d-values.
+template <typename T, int HD>
+DEV void stage_transposed(char* lds, const T* base, int64_t ld, int row0, int nrows, int tid) {
+  using G = AttnGeom<T, HD>;
+  constexpr int TASKS = (BKV / 4) * G::CPR;
+  for (int t = tid; t < TASKS; t += THREADS) {
+    const int rq = t / G::CPR, ch = t % G::CPR;
+    u32x4 v[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int r = row0 + rq * 4 + j;
+      v[j] = r < nrows ? ld16(base + (int64_t)r * ld + ch * G::VE) : u32x4{0, 0, 0, 0};
+    }
+    if constexpr (sizeof(T) == 2) {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const int w = e >> 1;
+        uint32_t q0, q1;
+        if (e & 1) {
+          q0 = (v[0][w] >> 16) | (v[1][w] & 0xffff0000u);
+          q1 = (v[2][w] >> 16) | (v[3][w] & 0xffff0000u);
+        } else {
+          q0 = (v[0][w] & 0xffffu) | (v[1][w] << 16);
+          q1 = (v[2][w] & 0xffffu) | (v[3][w] << 16);
+        }
+        st8(lds + (ch * 8 + e) * G::TP + rq * 8, u32x2{q0, q1});
+      }
+    } else {
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        st16(lds + (ch * 4 + e) * G::TP + rq * 16, u32x4{v[0][e], v[1][e], v[2][e], v[3][e]});
+    }
+  }
+}
+
+// Load this lane's head row (row `row`, zero if out of range) as NS B-operand fragments.
+template <typename T, int HD, int NS = AttnGeom<T, HD>::NS>
+DEV void load_row_frags(u32x4 (&f)[NS], const T* base, int64_t ld, int row, int nrows, int h) {
+  using G = AttnGeom<T, HD>;
+#pragma unroll
+  for (int s = 0; s < G::NS; ++s)
+    f[s] = row < nrows ? ld16(base + (int64_t)row * ld + (2 * s + h) * G::VE) : u32x4{0, 0, 0, 0};
+}
+
+// acc (32 x 32) += rows [r0, r0+32) of a row-layout LDS tile (A operand) times fragments f.
+template <typename T, int HD, int NS = AttnGeom<T, HD>::NS>
+DEV void mma_rows(f32x16& acc, const char* lds, int r0, const u32x4 (&f)[NS], int h, int l32) {
+  using G = AttnGeom<T, HD>;
+#pragma unroll
+  for (int s = 0; s < G::NS; ++s) {
+    const u32x4 a = *reinterpret_cast<const u32x4*>(lds + (r0 + l32) * G::RP + (2 * s + h) * 16);
+    Mfma<T>::mma(acc, a, f[s]);
+  }
+}
+
+// out[db] (HD x 32) += Xt[d][c0 .. c0+32) (transposed LDS tile, A operand) times the 32x32
+// probability-like matrix p held in MFMA result layout (B operand: lane column, 16 rows).
+template <typename T, int HD, int DB = AttnGeom<T, HD>::DB>
+DEV void mma_transposed(f32x16 (&out)[DB], const char* ldst, int c0, const float (&p)[16], int h,
+                        int l32) {
+  using G = AttnGeom<T, HD>;
+  if constexpr (sizeof(T) == 2) {
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      u32x4 b{pack_bf16(p[8 * u], p[8 * u + 1]), pack_bf16(p[8 * u + 2], p[8 * u + 3]),
+              pack_bf16(p[8 * u + 4], p[8 * u + 5]), pack_bf16(p[8 * u + 6], p[8 * u + 7])};
+      const int ca = c0 + 16 * u + 4 * h;  // slots 8u..8u+3 -> columns ca..ca+3; +8 for the rest
+#pragma unroll
+      for (int db = 0; db < HD / 32; ++db) {
+        const char* row = ldst + (db * 32 + l32) * G::TP;
+        const u32x2 lo = *reinterpret_cast<const u32x2*>(row + ca * 2);
+        const u32x2 hi = *reinterpret_cast<const u32x2*>(row + (ca + 8) * 2);
+        Mfma<T>::mma(out[db], u32x4{lo[0], lo[1], hi[0], hi[1]}, b);
+      }
+      if constexpr (HD == 16) {
+        // 16 rows of head_dim: lanes 16..31 of the A operand read zero rows
+        const char* row = ldst + (l32 & 15) * G::TP;
+        u32x4 a{0, 0, 0, 0};
+        if (l32 < 16) {
+          const u32x2 lo = *reinterpret_cast<const u32x2*>(row + ca * 2);
+          const u32x2 hi = *reinterpret_cast<const u32x2*>(row + (ca + 8) * 2);
+          a = u32x4{lo[0], lo[1], hi[0], hi[1]};
+        }
+        Mfma<T>::mma(out[0], a, b);
+      }
+    }
+  } else {
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const u32x4 b{__builtin_bit_cast(uint32_t, p[4 * u]), __builtin_bit_cast(uint32_t, p[4 * u + 1]),
+                    __builtin_bit_cast(uint32_t, p[4 * u + 2]),
+                    __builtin_bit_cast(uint32_t, p[4 * u + 3])};
+      const int ca = c0 + 8 * u + 4 * h;
+#pragma unroll
+      for (int db = 0; db < HD / 32; ++db) {
+        const char* row = ldst + (db * 32 + l32) * G::TP;
+        Mfma<T>::mma(out[db], *reinterpret_cast<const u32x4*>(row + ca * 4), b);
+      }
+      if constexpr (HD == 16) {
+        u32x4 a{0, 0, 0, 0};
+        if (l32 < 16) a = *reinterpret_cast<const u32x4*>(ldst + l32 * G::TP + ca * 4);
+        Mfma<T>::mma(out[0], a, b);
+      }
+    }
+  }
+}
+
+// Store a (HD x 32) result held transposed in MFMA layout (lane = column `row`, registers = d)
+// into row `row` of a head slice: dst + row * ld + d.
+template <typename T, int HD, int DB = AttnGeom<T, HD>::DB>
+DEV void store_head_row(const f32x16 (&acc)[DB], T* dst, int64_t ld, int row, int nrows,
+                        float scale, int h, int l32) {
+  if (row >= nrows) return;
+  T* out = dst + (int64_t)row * ld;
+#pragma unroll
+  for (int db = 0; db < DB; ++db) {
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+      const int d = db * 32 + g * 8 + h * 4;  // rows mfma_row(4g .. 4g+3, h)
+      if (HD == 16 && d >= 16) continue;
+      float v[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) v[e] = acc[db][4 * g + e] * scale;
+      if constexpr (sizeof(T) == 2)
+        st8(out + d, u32x2{pack_bf16(v[0], v[1]), pack_bf16(v[2], v[3])});
+      else
+        st16(out + d, u32x4{__builtin_bit_cast(uint32_t, v[0]), __builtin_bit_cast(uint32_t, v[1]),
+                            __builtin_bit_cast(uint32_t, v[2]), __builtin_bit_cast(uint32_t, v[3])});
+    }
+  }
+}
+
+// ----------------------------------------------------------------------------------- forward
+template <typename T, int HD>
+__global__ __launch_bounds__(THREADS) void attn_fwd_kernel(const T* __restrict__ qkv,
+                                                           T* __restrict__ out,
+                                                           float* __restrict__ lse, int T_,
+                                                           int H) {
+  using G = AttnGeom<T, HD>;
+  __shared__ __attribute__((aligned(16))) char ks[BKV * G::RP];
+  __shared__ __attribute__((aligned(16))) char vt[HD * G::TP];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, h = lane >> 5, l32 = lane & 31;
+  const int nqb = (T_ + 127) / 128;
+  const int qb = nqb - 1 - (int)blockIdx.x;  // heaviest query blocks first
+  const int bh = blockIdx.y, b = bh / H, hh = bh % H;
+  const int dm = H * HD;
+  const int64_t ld = 3 * (int64_t)dm;
+  const T* Q = qkv + (int64_t)b * T_ * ld + hh * HD;
+  const T* K = Q + dm;
+  const T* V = Q + 2 * dm;
+
+  const int q0 = qb * 128;
+  const int qw = q0 + wave * 32;  // this wave's first query
+  const int qi = qw + l32;        // this lane's query
+  u32x4 qf[G::NS];
+  load_row_frags<T, HD>(qf, Q, ld, qi, T_, h);
+
+  f32x16 o[G::DB];
+#pragma unroll
+  for (int i = 0; i < G::DB; ++i) o[i] = f32x16{};
+  float m_run = -INFINITY, l_run = 0.0f;
+  const float c = LOG2E / sqrtf((float)HD);
+
+  const int kv_end = min(T_, q0 + 128);
+  for (int kv0 = 0; kv0 < kv_end; kv0 += BKV) {
+    __syncthreads();
+    stage_rows<T, HD>(ks, K, ld, kv0, T_, tid);
+    stage_transposed<T, HD>(vt, V, ld, kv0, T_, tid);
+    __syncthreads();
+#pragma unroll
+    for (int jb = 0; jb < 2; ++jb) {
+      const int j0 = kv0 + jb * 32;
+      if (j0 > qw + 31 || j0 >= T_) continue;  // fully masked for this wave
+      f32x16 s = f32x16{};
+      mma_rows<T, HD>(s, ks, jb * 32, qf, h, l32);
+      float p[16];
+      float mloc = -INFINITY;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int j = j0 + mfma_row(r, h);
+        p[r] = (j > qi || j >= T_) ? -INFINITY : s[r] * c;
+        mloc = fmaxf(mloc, p[r]);
+      }
+      mloc = fmaxf(mloc, __shfl_xor(mloc, 32, 64));
+      const float m_new = fmaxf(m_run, mloc);
+      const float alpha = exp2f(m_run - m_new);
+      float lsum = 0.0f;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        p[r] = exp2f(p[r] - m_new);
+        lsum += p[r];
+      }
+      l_run = l_run * alpha + lsum;
+      m_run = m_new;
+#pragma unroll
+      for (int i = 0; i < G::DB; ++i) o[i] *= alpha;
+      mma_transposed<T, HD>(o, vt, jb * 32, p, h, l32);
+    }
+  }
+  const float l_tot = l_run + __shfl_xor(l_run, 32, 64);
+  store_head_row<T, HD>(o, out + (int64_t)b * T_ * dm + hh * HD, dm, qi, T_, 1.0f / l_tot, h, l32);
+  if (h == 0 && qi < T_) lse[(int64_t)bh * T_ + qi] = (m_run + log2f(l_tot)) * LN2;
+}
+
+// --------------------------------------------------------------------- backward: D = rowsum
+template <typename T, int HD>
+__global__ void attn_dsum_kernel(const T* __restrict__ out, const T* __restrict__ dout,
+                                 float* __restrict__ dsum, int T_, int H, int rows) {
+  constexpr int VE = 16 / (int)sizeof(T);
+  constexpr int LPH = HD / VE;  // lanes per head
+  const int lane = threadIdx.x & 63;
+  const int row = blockIdx.x * (blockDim.x / 64) + (threadIdx.x >> 6);
+  if (row >= rows) return;
+  const int dm = H * HD;
+  const int b = row / T_, t = row % T_;
+  for (int v0 = 0; v0 < dm / VE; v0 += 64) {
+    const int v = v0 + lane;
+    float s = 0.0f;
+    if (v < dm / VE) {
+      float a[VE], g[VE];
+      Vec<T>::unpack(ld16(out + (int64_t)row * dm + v * VE), a);
+      Vec<T>::unpack(ld16(dout + (int64_t)row * dm + v * VE), g);
+#pragma unroll
+      for (int e = 0; e < VE; ++e) s += a[e] * g[e];
+    }
+#pragma unroll
+    for (int o = 1; o < LPH; o <<= 1) s += __shfl_xor(s, o, 64);
+    if (v < dm / VE && (v % LPH) == 0) {
+      const int hh = v / LPH;
+      dsum[((int64_t)b * H + hh) * T_ + t] = s;
+    }
+  }
+}
+
+// ------------------------------------------------------------------- backward: dK and dV
+template <typename T, int HD>
+__global__ __launch_bounds__(THREADS) void attn_bwd_dkdv_kernel(
+    const T* __restrict__ qkv, const T* __restrict__ dout, const float* __restrict__ lse,
+    const float* __restrict__ dsum, T* __restrict__ dqkv, int T_, int H) {
+  using G = AttnGeom<T, HD>;
+  __shared__ __attribute__((aligned(16))) char qs[BKV * G::RP];
+  __shared__ __attribute__((aligned(16))) char dos[BKV * G::RP];
+  __shared__ __attribute__((aligned(16))) char qt[HD * G::TP];
+  __shared__ __attribute__((aligned(16))) char dot[HD * G::TP];
+  __shared__ float lse_s[BKV], d_s[BKV];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, h = lane >> 5, l32 = lane & 31;
+  const int nkb = (T_ + 127) / 128;
+  const int kb = (int)blockIdx.x;  // key blocks near the start see the most queries
+  const int bh = blockIdx.y, b = bh / H, hh = bh % H;
+  const int dm = H * HD;
+  const int64_t ld = 3 * (int64_t)dm;
+  const T* Q = qkv + (int64_t)b * T_ * ld + hh * HD;
+  const T* K = Q + dm;
+  const T* V = Q + 2 * dm;
+  const T* dO = dout + (int64_t)b * T_ * dm + hh * HD;
+  const float* lse_bh = lse + (int64_t)bh * T_;
+  const float* d_bh = dsum + (int64_t)bh * T_;
+  (void)nkb;
+
+  const int k0 = kb * 128;
+  const int kw = k0 + wave * 32;
+  const int kj = kw + l32;  // this lane's key
+  u32x4 kf[G::NS], vf[G::NS];
+  load_row_frags<T, HD>(kf, K, ld, kj, T_, h);
+  load_row_frags<T, HD>(vf, V, ld, kj, T_, h);
+  f32x16 dv[G::DB], dk[G::DB];
+#pragma unroll
+  for (int i = 0; i < G::DB; ++i) dv[i] = dk[i] = f32x16{};
+  const float c = LOG2E / sqrtf((float)HD);
+
+  for (int i0 = (k0 / BKV) * BKV; i0 < T_; i0 += BKV) {
+    __syncthreads();
+    stage_rows<T, HD>(qs, Q, ld, i0, T_, tid);
+    stage_rows<T, HD>(dos, dO, dm, i0, T_, tid);
+    stage_transposed<T, HD>(qt, Q, ld, i0, T_, tid);
+    stage_transposed<T, HD>(dot, dO, dm, i0, T_, tid);
+    if (tid < BKV) {
+      const int i = i0 + tid;
+      lse_s[tid] = i < T_ ? lse_bh[i] * LOG2E : 0.0f;
+      d_s[tid] = i < T_ ? d_bh[i] : 0.0f;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int ib = 0; ib < 2; ++ib) {
+      const int iq = i0 + ib * 32;
+      if (iq + 31 < kw || iq >= T_) continue;  // all queries before this wave's keys
+      f32x16 s = f32x16{}, dp = f32x16{};
+      mma_rows<T, HD>(s, qs, ib * 32, kf, h, l32);
+      mma_rows<T, HD>(dp, dos, ib * 32, vf, h, l32);
+      float p[16], ds[16];
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const int il = ib * 32 + g * 8 + h * 4;
+        const f32x4 lv = *reinterpret_cast<const f32x4*>(lse_s + il);
+        const f32x4 dd = *reinterpret_cast<const f32x4*>(d_s + il);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int r = 4 * g + e;
+          const int i = i0 + il + e;
+          const float pr = (i < kj || i >= T_) ? 0.0f : exp2f(s[r] * c - lv[e]);
+          p[r] = pr;
+          ds[r] = pr * (dp[r] - dd[e]);
+        }
+      }
+      mma_transposed<T, HD>(dv, dot, ib * 32, p, h, l32);
+      mma_transposed<T, HD>(dk, qt, ib * 32, ds, h, l32);
+    }
+  }
+  T* dK = dqkv + (int64_t)b * T_ * ld + dm + hh * HD;
+  store_head_row<T, HD>(dk, dK, ld, kj, T_, 1.0f / sqrtf((float)HD), h, l32);
+  store_head_row<T, HD>(dv, dK + dm, ld, kj, T_, 1.0f, h, l32);
+}
+
+// ----------------------------------------------------------------------- backward: dQ
+template <typename T, int HD>
+__global__ __launch_bounds__(THREADS) void attn_bwd_dq_kernel(
+    const T* __restrict__ qkv, const T* __restrict__ dout, const float* __restrict__ lse,
+    const float* __restrict__ dsum, T* __restrict__ dqkv, int T_, int H) {
+  using G = AttnGeom<T, HD>;
+  __shared__ __attribute__((aligned(16))) char ks[BKV * G::RP];
+  __shared__ __attribute__((aligned(16))) char vs[BKV * G::RP];
+  __shared__ __attribute__((aligned(16))) char kt[HD * G::TP];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, h = lane >> 5, l32 = lane & 31;
+  const int nqb = (T_ + 127) / 128;
+  const int qb = nqb - 1 - (int)blockIdx.x;
+  const int bh = blockIdx.y, b = bh / H, hh = bh % H;
+  const int dm = H * HD;
+  const int64_t ld = 3 * (int64_t)dm;
+  const T* Q = qkv + (int64_t)b * T_ * ld + hh * HD;
+  const T* K = Q + dm;
+  const T* V = Q + 2 * dm;
+  const T* dO = dout + (int64_t)b * T_ * dm + hh * HD;
+
+  const int q0 = qb * 128;
+  const int qw = q0 + wave * 32;
+  const int qi = qw + l32;
+  u32x4 qf[G::NS], df[G::NS];
+  load_row_frags<T, HD>(qf, Q, ld, qi, T_, h);
+  load_row_frags<T, HD>(df, dO, dm, qi, T_, h);
+  const float lse_i = qi < T_ ? lse[(int64_t)bh * T_ + qi] * LOG2E : 0.0f;
+  const float d_i = qi < T_ ? dsum[(int64_t)bh * T_ + qi] : 0.0f;
+  f32x16 dq[G::DB];
+#pragma unroll
+  for (int i = 0; i < G::DB; ++i) dq[i] = f32x16{};
+  const float c = LOG2E / sqrtf((float)HD);
+
+  const int kv_end = min(T_, q0 + 128);
+  for (int kv0 = 0; kv0 < kv_end; kv0 += BKV) {
+    __syncthreads();
+    stage_rows<T, HD>(ks, K, ld, kv0, T_, tid);
+    stage_rows<T, HD>(vs, V, ld, kv0, T_, tid);
+    stage_transposed<T, HD>(kt, K, ld, kv0, T_, tid);
+    __syncthreads();
+#pragma unroll
+    for (int jb = 0; jb < 2; ++jb) {
+      const int j0 = kv0 + jb * 32;
+      if (j0 > qw + 31 || j0 >= T_) continue;
+      f32x16 s = f32x16{}, dp = f32x16{};
+      mma_rows<T, HD>(s, ks, jb * 32, qf, h, l32);
+      mma_rows<T, HD>(dp, vs, jb * 32, df, h, l32);
+      float ds[16];
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int j = j0 + mfma_row(r, h);
+        const float pr = (j > qi || j >= T_) ? 0.0f : exp2f(s[r] * c - lse_i);
+        ds[r] = pr * (dp[r] - d_i);
+      }
+      mma_transposed<T, HD>(dq, kt, jb * 32, ds, h, l32);
+    }
+  }
+  store_head_row<T, HD>(dq, dqkv + (int64_t)b * T_ * ld + hh * HD, ld, qi, T_,
+                        1.0f / sqrtf((float)HD), h, l32);
+}
+
+template <typename T, int HD>
+hipError_t fwd_t(int B, int T_, int H, const void* qkv, void* out, float* lse, hipStream_t s) {
+  dim3 grid((T_ + 127) / 128, B * H);
+  hipLaunchKernelGGL((attn_fwd_kernel<T, HD>), grid, dim3(THREADS), 0, s,
+                     static_cast<const T*>(qkv), static_cast<T*>(out), lse, T_, H);
+  return hipGetLastError();
+}
+
+template <typename T, int HD>
+hipError_t bwd_t(int B, int T_, int H, const void* qkv, const void* out, const float* lse,
+                 const void* dout, void* dqkv, float* dsum, hipStream_t s) {
+  const int rows = B * T_;
+  hipLaunchKernelGGL((attn_dsum_kernel<T, HD>), dim3((rows + 3) / 4), dim3(256), 0, s,
+                     static_cast<const T*>(out), static_cast<const T*>(dout), dsum, T_, H, rows);
+  dim3 grid((T_ + 127) / 128, B * H);
+  hipLaunchKernelGGL((attn_bwd_dkdv_kernel<T, HD>), grid, dim3(THREADS), 0, s,
+                     static_cast<const T*>(qkv), static_cast<const T*>(dout), lse, dsum,
+                     static_cast<T*>(dqkv), T_, H);
+  hipLaunchKernelGGL((attn_bwd_dq_kernel<T, HD>), grid, dim3(THREADS), 0, s,
+                     static_cast<const T*>(qkv), static_cast<const T*>(dout), lse, dsum,
+                     static_cast<T*>(dqkv), T_, H);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_attn_fwd(bool is_bf16, int B, int T, int H, int hd, const void* qkv, void* out,
+                           float* lse, hipStream_t s) {
+  if (B * T == 0) return hipSuccess;
+  if (is_bf16) {
+    if (hd == 64) return fwd_t<bf16, 64>(B, T, H, qkv, out, lse, s);
+    if (hd == 32) return fwd_t<bf16, 32>(B, T, H, qkv, out, lse, s);
+    if (hd == 16) return fwd_t<bf16, 16>(B, T, H, qkv, out, lse, s);
+  } else {
+    if (hd == 64) return fwd_t<float, 64>(B, T, H, qkv, out, lse, s);
+    if (hd == 32) return fwd_t<float, 32>(B, T, H, qkv, out, lse, s);
+    if (hd == 16) return fwd_t<float, 16>(B, T, H, qkv, out, lse, s);
+  }
+  return hipErrorInvalidValue;
+}
+
+hipError_t launch_attn_bwd(bool is_bf16, int B, int T, int H, int hd, const void* qkv,
+                           const void* out, const float* lse, const void* dout, void* dqkv,
+                           float* dsum, hipStream_t s) {
+  if (B * T == 0) return hipSuccess;
+  if (is_bf16) {
+    if (hd == 64) return bwd_t<bf16, 64>(B, T, H, qkv, out, lse, dout, dqkv, dsum, s);
+    if (hd == 32) return bwd_t<bf16, 32>(B, T, H, qkv, out, lse, dout, dqkv, dsum, s);
+    if (hd == 16) return bwd_t<bf16, 16>(B, T, H, qkv, out, lse, dout, dqkv, dsum, s);
+  } else {
+    if (hd == 64) return bwd_t<float, 64>(B, T, H, qkv, out, lse, dout, dqkv, dsum, s);
+    if (hd == 32) return bwd_t<float, 32>(B, T, H, qkv, out, lse, dout, dqkv, dsum, s);
+    if (hd == 16) return bwd_t<float, 16>(B, T, H, qkv, out, lse, dout, dqkv, dsum, s);
+  }
+  return hipErrorInvalidValue;
+}

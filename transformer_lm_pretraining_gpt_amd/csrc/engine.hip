@@ -1,0 +1,740 @@
+// Engine and C ABI of libgpt2.so: configuration checks, the arena layout, and the launch
+// sequences of one GPT-2 training step (forward + loss, backward, AdamW) on one HIP stream.
+//
+// The model is GPT-2's pre-LN decoder ("Criei GPT-2 do zero com uma RTX 4090", sections "Ambiente"
+// and "Configuração do treinamento": GPT-2 small built the nanoGPT way, vocabulary padded to a
+// multiple of 128) trained on next-token cross-entropy with AdamW ("Pré-treinar um LLM: dados,
+// compute, leis de escala e custo", opening paragraph). Everything below only sequences kernels;
+// all arithmetic of the step runs in the .hip kernel files.
+#include <math.h>
+#include <string.h>
+
+#include <algorithm>
+#include <string>
+#include <vector>
+
+#include "../../include/gpt2.h"
+#include "common.h"
+#include "kernels.h"
+
+namespace {
+
+thread_local std::string g_err = "no error";
+
+gpt2_status fail(gpt2_status s, const std::string& msg) {
+  g_err = msg;
+  return s;
+}
+
+#define HIPCHK(x)                                                                  \
+  do {                                                                             \
+    hipError_t e_ = (x);                                                           \
+    if (e_ != hipSuccess)                                                          \
+      return fail(GPT2_E_HIP, std::string(#x) + " failed: " + hipGetErrorString(e_)); \
+  } while (0)
+
+constexpr int LN_ROWS_PER_BLOCK = 64;
+constexpr int COLSUM_ROWS_PER_BLOCK = 64;
+constexpr int MAX_ROWS = 16384;
+constexpr int TIMING_CAP = 4096;
+
+// ------------------------------------------------------------------------------ geometry
+struct Geo {
+  int L, d, H, hd, T, B, M, V, Vp;
+  bool bf16;
+  int64_t N, P_layer;
+  int64_t wte, wpe, layer0, lnfg, lnfb;
+  int64_t lay(int l) const { return layer0 + (int64_t)l * P_layer; }
+  int64_t ln1g(int l) const { return lay(l); }
+  int64_t ln1b(int l) const { return lay(l) + d; }
+  int64_t wqkv(int l) const { return lay(l) + 2 * (int64_t)d; }
+  int64_t bqkv(int l) const { return wqkv(l) + 3 * (int64_t)d * d; }
+  int64_t wo(int l) const { return bqkv(l) + 3 * (int64_t)d; }
+  int64_t bo(int l) const { return wo(l) + (int64_t)d * d; }
+  int64_t ln2g(int l) const { return bo(l) + d; }
+  int64_t ln2b(int l) const { return ln2g(l) + d; }
+  int64_t wfc(int l) const { return ln2b(l) + d; }
+  int64_t bfc(int l) const { return wfc(l) + 4 * (int64_t)d * d; }
+  int64_t wproj(int l) const { return bfc(l) + 4 * (int64_t)d; }
+  int64_t bproj(int l) const { return wproj(l) + 4 * (int64_t)d * d; }
+};
+
+bool validate(const gpt2_config* c, std::string& why) {
+  if (!c) { why = "config is NULL"; return false; }
+  if (c->n_layer < 1 || c->d_model < 1 || c->n_head < 1 || c->seq_len < 1 || c->batch < 1) {
+    why = "n_layer, d_model, n_head, seq_len and batch must be >= 1"; return false;
+  }
+  if (c->d_model % c->n_head) { why = "d_model must be divisible by n_head"; return false; }
+  if (c->vocab < 1 || c->vocab_padded < c->vocab) { why = "need 1 <= vocab <= vocab_padded"; return false; }
+  if (c->vocab_padded > 65536) { why = "vocab_padded must be <= 65536"; return false; }
+  if (c->precision != GPT2_FP32 && c->precision != GPT2_BF16) { why = "unknown precision"; return false; }
+  if (c->reserved != 0) { why = "reserved must be 0"; return false; }
+  if (!(c->init_std >= 0.0f) || !isfinite(c->init_std)) { why = "init_std must be finite and >= 0"; return false; }
+  return true;
+}
+
+// Valid but outside the kernels' coverage.
+bool supported(const gpt2_config* c, std::string& why) {
+  const int hd = c->d_model / c->n_head;
+  if (hd != 16 && hd != 32 && hd != 64) { why = "head_dim must be 16, 32 or 64"; return false; }
+  if (c->d_model % 8) { why = "d_model must be a multiple of 8"; return false; }
+  if (c->d_model > 2048) { why = "d_model must be <= 2048"; return false; }
+  if (c->vocab_padded % 8) { why = "vocab_padded must be a multiple of 8"; return false; }
+  if ((int64_t)c->batch * c->seq_len > MAX_ROWS) { why = "batch * seq_len must be <= 16384"; return false; }
+  if (c->precision == GPT2_FP32 && c->vocab_padded > 32768) {
+    why = "fp32 precision supports vocab_padded <= 32768"; return false;
+  }
+  return true;
+}
+
+Geo geometry(const gpt2_config* c) {
+  Geo g;
+  g.L = c->n_layer; g.d = c->d_model; g.H = c->n_head; g.hd = g.d / g.H;
+  g.T = c->seq_len; g.B = c->batch; g.M = g.B * g.T; g.V = c->vocab; g.Vp = c->vocab_padded;
+  g.bf16 = c->precision == GPT2_BF16;
+  const int64_t d = g.d;
+  g.P_layer = 12 * d * d + 13 * d;
+  g.wte = 0;
+  g.wpe = (int64_t)g.Vp * d;
+  g.layer0 = g.wpe + (int64_t)g.T * d;
+  g.lnfg = g.layer0 + g.L * g.P_layer;
+  g.lnfb = g.lnfg + d;
+  g.N = g.lnfb + d;
+  return g;
+}
+
+// Tensors in canonical order: (offset, count, is_matrix, is_ln_gain)
+struct Tensor { int64_t off, count; bool matrix, gain; };
+std::vector<Tensor> tensors(const Geo& g) {
+  std::vector<Tensor> t;
+  const int64_t d = g.d;
+  t.push_back({g.wte, (int64_t)g.Vp * d, true, false});
+  t.push_back({g.wpe, (int64_t)g.T * d, true, false});
+  for (int l = 0; l < g.L; ++l) {
+    t.push_back({g.ln1g(l), d, false, true});
+    t.push_back({g.ln1b(l), d, false, false});
+    t.push_back({g.wqkv(l), 3 * d * d, true, false});
+    t.push_back({g.bqkv(l), 3 * d, false, false});
+    t.push_back({g.wo(l), d * d, true, false});
+    t.push_back({g.bo(l), d, false, false});
+    t.push_back({g.ln2g(l), d, false, true});
+    t.push_back({g.ln2b(l), d, false, false});
+    t.push_back({g.wfc(l), 4 * d * d, true, false});
+    t.push_back({g.bfc(l), 4 * d, false, false});
+    t.push_back({g.wproj(l), 4 * d * d, true, false});
+    t.push_back({g.bproj(l), d, false, false});
+  }
+  t.push_back({g.lnfg, d, false, true});
+  t.push_back({g.lnfb, d, false, false});
+  return t;
+}
+
+std::vector<AdamSeg> decay_segments(const Geo& g) {
+  std::vector<AdamSeg> s;
+  for (const Tensor& t : tensors(g)) {
+    const int dec = t.matrix ? 1 : 0;
+    if (s.empty() || s.back().decay != dec) s.push_back({t.off, dec, 0});
+  }
+  return s;
+}
+
+// ------------------------------------------------------------------------------ GEMM plans
+int pick_tile(const Geo& g, int M, int N) {
+  if (!g.bf16) return TILE_128;
+  const int64_t t256 = (int64_t)((M + 255) / 256) * ((N + 255) / 256);
+  const int64_t t256x128 = (int64_t)((M + 255) / 256) * ((N + 127) / 128);
+  if (t256 >= 512) return TILE_256;
+  if (t256x128 >= 256) return TILE_256x128;
+  return TILE_128;
+}
+
+// Split of the K = rows reduction of a weight gradient (in x out): enough blocks for 256 CUs.
+struct Split { int splits, k_split; };
+Split pick_split(const Geo& g, int in, int out) {
+  const int kt = gemm_k_tile(g.bf16);
+  const int64_t tiles = (int64_t)((in + 127) / 128) * ((out + 127) / 128);
+  int s = (int)((512 + tiles - 1) / tiles);
+  if (s < 1) s = 1;
+  if (s > 8) s = 8;
+  int per = (g.M + s - 1) / s;
+  per = (per + kt - 1) / kt * kt;
+  if (per < kt) per = kt;
+  s = (g.M + per - 1) / per;
+  return {s, per};
+}
+
+// ------------------------------------------------------------------------------ buffers
+struct Bufs {
+  float *params = nullptr, *grads = nullptr, *m = nullptr, *v = nullptr;
+  void* shadow = nullptr;
+  AdamSeg* segs = nullptr;
+  std::vector<float*> resid, resid_mid, ln1_mean, ln1_rstd, ln2_mean, ln2_rstd, lse;
+  std::vector<void*> ln1, qkv, att, ln2, fc, act;
+  void* lnf = nullptr;
+  float *lnf_mean = nullptr, *lnf_rstd = nullptr;
+  void* logits = nullptr;
+  float *row_loss = nullptr, *loss = nullptr;
+  int* err = nullptr;
+  float* dres = nullptr;
+  void* dres_t = nullptr;
+  float* dtmp = nullptr;
+  void *dbig = nullptr, *dqkv = nullptr, *datt = nullptr;
+  float* dsum = nullptr;
+  float* colpart = nullptr;
+  float* splitk = nullptr;
+  uint32_t* keys = nullptr;
+  float* segpart = nullptr;
+};
+
+struct Carver {
+  uintptr_t base;
+  size_t off = 0;
+  template <typename P>
+  P* take(size_t bytes) {
+    off = (off + 255) & ~(size_t)255;
+    P* p = reinterpret_cast<P*>(base + off);
+    off += bytes;
+    return p;
+  }
+};
+
+size_t carve(const Geo& g, uintptr_t base, Bufs& b) {
+  Carver c{base};
+  const size_t ts = g.bf16 ? 2 : 4;
+  const size_t N = (size_t)g.N, M = (size_t)g.M, d = (size_t)g.d;
+  b.params = c.take<float>(4 * N);
+  b.grads = c.take<float>(4 * N);
+  b.m = c.take<float>(4 * N);
+  b.v = c.take<float>(4 * N);
+  b.shadow = g.bf16 ? c.take<void>(2 * N) : nullptr;
+  b.segs = c.take<AdamSeg>(sizeof(AdamSeg) * decay_segments(g).size());
+  const size_t bht = (size_t)g.B * g.H * g.T;
+  b.resid.resize(g.L + 1);
+  b.resid_mid.resize(g.L);
+  b.ln1.resize(g.L); b.qkv.resize(g.L); b.att.resize(g.L); b.ln2.resize(g.L);
+  b.fc.resize(g.L); b.act.resize(g.L);
+  b.ln1_mean.resize(g.L); b.ln1_rstd.resize(g.L); b.ln2_mean.resize(g.L); b.ln2_rstd.resize(g.L);
+  b.lse.resize(g.L);
+  for (int l = 0; l <= g.L; ++l) b.resid[l] = c.take<float>(4 * M * d);
+  for (int l = 0; l < g.L; ++l) {
+    b.resid_mid[l] = c.take<float>(4 * M * d);
+    b.ln1[l] = c.take<void>(ts * M * d);
+    b.ln1_mean[l] = c.take<float>(4 * M);
+    b.ln1_rstd[l] = c.take<float>(4 * M);
+    b.qkv[l] = c.take<void>(ts * M * 3 * d);
+    b.att[l] = c.take<void>(ts * M * d);
+    b.lse[l] = c.take<float>(4 * bht);
+    b.ln2[l] = c.take<void>(ts * M * d);
+    b.ln2_mean[l] = c.take<float>(4 * M);
+    b.ln2_rstd[l] = c.take<float>(4 * M);
+    b.fc[l] = c.take<void>(ts * M * 4 * d);
+    b.act[l] = c.take<void>(ts * M * 4 * d);
+  }
+  b.lnf = c.take<void>(ts * M * d);
+  b.lnf_mean = c.take<float>(4 * M);
+  b.lnf_rstd = c.take<float>(4 * M);
+  b.logits = c.take<void>(ts * M * (size_t)g.Vp);
+  b.row_loss = c.take<float>(4 * M);
+  b.loss = c.take<float>(4);
+  b.err = c.take<int>(4);
+  b.dres = c.take<float>(4 * M * d);
+  b.dres_t = c.take<void>(ts * M * d);
+  b.dtmp = c.take<float>(4 * M * d);
+  b.dbig = c.take<void>(ts * M * 4 * d);
+  b.dqkv = c.take<void>(ts * M * 3 * d);
+  b.datt = c.take<void>(ts * M * d);
+  b.dsum = c.take<float>(4 * bht);
+  const size_t nblk = (size_t)ln_bwd_blocks(g.M, LN_ROWS_PER_BLOCK);
+  const size_t ncs = (M + COLSUM_ROWS_PER_BLOCK - 1) / COLSUM_ROWS_PER_BLOCK;
+  b.colpart = c.take<float>(4 * std::max(nblk * 3 * d, ncs * 4 * d));
+  size_t sk = 0;
+  const int shapes[4][2] = {{g.d, 3 * g.d}, {g.d, g.d}, {g.d, 4 * g.d}, {4 * g.d, g.d}};
+  for (auto& s : shapes) {
+    const Split sp = pick_split(g, s[0], s[1]);
+    if (sp.splits > 1) sk = std::max(sk, (size_t)sp.splits * s[0] * s[1]);
+  }
+  b.splitk = c.take<float>(4 * std::max<size_t>(sk, 1));
+  b.keys = c.take<uint32_t>(4 * M);
+  b.segpart = c.take<float>(4 * (size_t)embed_bwd_chunks(g.M) * 2 * d);
+  return (c.off + 255) & ~(size_t)255;
+}
+
+}  // namespace
+
+// ------------------------------------------------------------------------------ context
+struct gpt2_ctx {
+  gpt2_config cfg;
+  Geo g;
+  Bufs b;
+  hipStream_t stream;
+  int64_t t = 0;
+  bool have_forward = false;
+  std::vector<AdamSeg> segs;
+  // timing
+  int timing_family = -1;
+  std::vector<hipEvent_t> ev;
+  int timed = 0;
+  double timed_work = 0.0;
+};
+
+namespace {
+
+// Records an event pair around one launch when its family is being timed.
+struct Timed {
+  gpt2_ctx* c;
+  bool on;
+  Timed(gpt2_ctx* c_, int family, double work) : c(c_), on(false) {
+    if (c->timing_family == family && c->timed < TIMING_CAP) {
+      on = true;
+      hipEventRecord(c->ev[2 * c->timed], c->stream);
+      c->timed_work += work;
+    }
+  }
+  ~Timed() {
+    if (on) {
+      hipEventRecord(c->ev[2 * c->timed + 1], c->stream);
+      ++c->timed;
+    }
+  }
+};
+
+enum { FAM_LMHEAD = 0, FAM_GEMM = 1, FAM_ATTN = 2, FAM_XENT = 3, FAM_ADAMW = 4 };
+
+const void* W(gpt2_ctx* c, int64_t off) {
+  return c->g.bf16 ? (const void*)(static_cast<const char*>(c->b.shadow) + 2 * off)
+                   : (const void*)(c->b.params + off);
+}
+
+gpt2_status gemm(gpt2_ctx* c, int a_kmajor, int b_kmajor, int M, int N, int K, const void* A,
+                 int64_t lda, const void* B, int64_t ldb, int epi, void* C, int64_t ldc,
+                 const float* bias = nullptr, const float* resid = nullptr, void* C2 = nullptr,
+                 const void* aux = nullptr, float alpha = 1.0f, float beta = 0.0f, int tag = 0) {
+  GemmParams p{};
+  p.A = A; p.lda = lda; p.B = B; p.ldb = ldb;
+  p.M = M; p.N = N; p.K = K; p.k_split = K;
+  p.epi = epi; p.C = C; p.ldc = ldc; p.c_split_stride = 0;
+  p.C2 = C2; p.bias = bias; p.resid = resid; p.aux = aux; p.alpha = alpha; p.beta = beta;
+  const double fl = 2.0 * M * N * K;
+  Timed t1(c, FAM_GEMM, fl);
+  Timed t0(c, tag == 1 ? FAM_LMHEAD : -2, fl);
+  HIPCHK(launch_gemm(c->g.bf16, a_kmajor, b_kmajor, pick_tile(c->g, M, N), 1, tag, p, c->stream));
+  return GPT2_OK;
+}
+
+// Weight gradient dW (in x out) = X^T dY over the M rows, X (M x in) and dY (M x out) row-major,
+// written (accumulate = 0) or added (1) into the fp32 gradient at gw.
+gpt2_status gemm_dw(gpt2_ctx* c, int in, int out, const void* X, const void* dY, float* gw,
+                    int accumulate) {
+  const Geo& g = c->g;
+  const Split sp = pick_split(g, in, out);
+  GemmParams p{};
+  p.A = X; p.lda = in; p.B = dY; p.ldb = out;
+  p.M = in; p.N = out; p.K = g.M; p.k_split = sp.k_split;
+  p.epi = EPI_F32; p.alpha = 1.0f;
+  Timed t1(c, FAM_GEMM, 2.0 * in * out * g.M);
+  if (sp.splits == 1) {
+    p.C = gw; p.ldc = out; p.beta = accumulate ? 1.0f : 0.0f;
+    HIPCHK(launch_gemm(g.bf16, 0, 0, TILE_128, 1, 0, p, c->stream));
+  } else {
+    p.C = c->b.splitk; p.ldc = out; p.c_split_stride = (int64_t)in * out; p.beta = 0.0f;
+    HIPCHK(launch_gemm(g.bf16, 0, 0, TILE_128, sp.splits, 0, p, c->stream));
+    HIPCHK(launch_splitk_reduce(c->b.splitk, sp.splits, (int64_t)in * out, in, out, gw, out, 1.0f,
+                                accumulate ? 1.0f : 0.0f, c->stream));
+  }
+  return GPT2_OK;
+}
+
+gpt2_status colsum(gpt2_ctx* c, const void* src, int N, float* out, int accumulate) {
+  const Geo& g = c->g;
+  const int nparts = (g.M + COLSUM_ROWS_PER_BLOCK - 1) / COLSUM_ROWS_PER_BLOCK;
+  HIPCHK(launch_colsum_partial(g.bf16, g.M, N, src, N, c->b.colpart, COLSUM_ROWS_PER_BLOCK,
+                               c->stream));
+  HIPCHK(launch_colsum_reduce(c->b.colpart, nparts, N, N, out, accumulate, c->stream));
+  return GPT2_OK;
+}
+
+// LayerNorm backward into the residual gradient, then its three column sums: gain and shift
+// gradients, and (when bias_out is not NULL) the bias gradient of the projection that produced
+// this residual stream.
+gpt2_status ln_backward(gpt2_ctx* c, const float* x, const float* mean, const float* rstd,
+                        int64_t g_off, int64_t b_off, float* bias_out, int has_dres,
+                        int accumulate) {
+  const Geo& g = c->g;
+  const int nblk = ln_bwd_blocks(g.M, LN_ROWS_PER_BLOCK);
+  HIPCHK(launch_ln_bwd(g.bf16, g.M, g.d, c->b.dtmp, x, mean, rstd, c->b.params + g_off, c->b.dres,
+                       has_dres, c->b.dres_t, c->b.colpart, LN_ROWS_PER_BLOCK, c->stream));
+  const int64_t stride = 3 * (int64_t)g.d;
+  HIPCHK(launch_colsum_reduce(c->b.colpart, nblk, stride, g.d, c->b.grads + g_off, accumulate,
+                              c->stream));
+  HIPCHK(launch_colsum_reduce(c->b.colpart + g.d, nblk, stride, g.d, c->b.grads + b_off,
+                              accumulate, c->stream));
+  if (bias_out)
+    HIPCHK(launch_colsum_reduce(c->b.colpart + 2 * g.d, nblk, stride, g.d, bias_out, accumulate,
+                                c->stream));
+  return GPT2_OK;
+}
+
+#define STEP(x)                          \
+  do {                                   \
+    gpt2_status s_ = (x);                \
+    if (s_ != GPT2_OK) return s_;        \
+  } while (0)
+
+gpt2_status forward(gpt2_ctx* c, const int32_t* tokens, const int32_t* targets, float* loss_user) {
+  const Geo& g = c->g;
+  Bufs& b = c->b;
+  float* P = b.params;
+  const int M = g.M, d = g.d;
+  HIPCHK(launch_embed_fwd(g.B, g.T, d, g.V, tokens, P + g.wte, P + g.wpe, b.resid[0], b.err,
+                          c->stream));
+  HIPCHK(launch_token_sort(M, g.V, tokens, b.keys, c->stream));
+  for (int l = 0; l < g.L; ++l) {
+    HIPCHK(launch_ln_fwd(g.bf16, M, d, b.resid[l], P + g.ln1g(l), P + g.ln1b(l), b.ln1[l],
+                         b.ln1_mean[l], b.ln1_rstd[l], c->stream));
+    STEP(gemm(c, 1, 0, M, 3 * d, d, b.ln1[l], d, W(c, g.wqkv(l)), 3 * d, EPI_STORE, b.qkv[l],
+              3 * d, P + g.bqkv(l)));
+    {
+      Timed t(c, FAM_ATTN, 4.0 * g.B * g.H * g.hd * ((double)g.T * (g.T + 1) / 2));
+      HIPCHK(launch_attn_fwd(g.bf16, g.B, g.T, g.H, g.hd, b.qkv[l], b.att[l], b.lse[l],
+                             c->stream));
+    }
+    STEP(gemm(c, 1, 0, M, d, d, b.att[l], d, W(c, g.wo(l)), d, EPI_BIAS_RESID, b.resid_mid[l], d,
+              P + g.bo(l), b.resid[l]));
+    HIPCHK(launch_ln_fwd(g.bf16, M, d, b.resid_mid[l], P + g.ln2g(l), P + g.ln2b(l), b.ln2[l],
+                         b.ln2_mean[l], b.ln2_rstd[l], c->stream));
+    STEP(gemm(c, 1, 0, M, 4 * d, d, b.ln2[l], d, W(c, g.wfc(l)), 4 * d, EPI_BIAS_GELU, b.fc[l],
+              4 * d, P + g.bfc(l), nullptr, b.act[l]));
+    STEP(gemm(c, 1, 0, M, d, 4 * d, b.act[l], 4 * d, W(c, g.wproj(l)), d, EPI_BIAS_RESID,
+              b.resid[l + 1], d, P + g.bproj(l), b.resid_mid[l]));
+  }
+  HIPCHK(launch_ln_fwd(g.bf16, M, d, b.resid[g.L], P + g.lnfg, P + g.lnfb, b.lnf, b.lnf_mean,
+                       b.lnf_rstd, c->stream));
+  STEP(gemm(c, 1, 1, M, g.Vp, d, b.lnf, d, W(c, g.wte), d, EPI_STORE, b.logits, g.Vp, nullptr,
+            nullptr, nullptr, nullptr, 1.0f, 0.0f, 1));
+  {
+    const double bytes = 2.0 * (g.bf16 ? 2 : 4) * (double)M * g.Vp;
+    Timed t(c, FAM_XENT, bytes);
+    HIPCHK(launch_xent(g.bf16, M, g.V, g.Vp, b.logits, targets, b.row_loss, b.err, c->stream));
+  }
+  HIPCHK(launch_loss_mean(M, b.row_loss, b.loss, loss_user, c->stream));
+  return GPT2_OK;
+}
+
+gpt2_status backward(gpt2_ctx* c, float grad_scale, int acc) {
+  const Geo& g = c->g;
+  Bufs& b = c->b;
+  float* G = b.grads;
+  const int M = g.M, d = g.d;
+  const float s = grad_scale / (float)M;
+  // LM head (tied): df = s * dz wte;  dwte = s * dz^T lnf (+ existing when accumulating)
+  STEP(gemm(c, 1, 0, M, d, g.Vp, b.logits, g.Vp, W(c, g.wte), d, EPI_F32, b.dtmp, d, nullptr,
+            nullptr, nullptr, nullptr, s, 0.0f));
+  {
+    GemmParams p{};
+    p.A = b.logits; p.lda = g.Vp; p.B = b.lnf; p.ldb = d;
+    p.M = g.Vp; p.N = d; p.K = M; p.k_split = M;
+    p.epi = EPI_F32; p.C = G + g.wte; p.ldc = d; p.alpha = s; p.beta = acc ? 1.0f : 0.0f;
+    Timed t(c, FAM_GEMM, 2.0 * g.Vp * d * M);
+    HIPCHK(launch_gemm(g.bf16, 0, 0, pick_tile(g, g.Vp, d), 1, 0, p, c->stream));
+  }
+  STEP(ln_backward(c, b.resid[g.L], b.lnf_mean, b.lnf_rstd, g.lnfg, g.lnfb, G + g.bproj(g.L - 1),
+                   0, acc));
+  for (int l = g.L - 1; l >= 0; --l) {
+    // h_{l+1} = h_mid + act W_proj + b_proj ; dres holds dh_{l+1}
+    STEP(gemm_dw(c, 4 * d, d, b.act[l], b.dres_t, G + g.wproj(l), acc));
+    STEP(gemm(c, 1, 1, M, 4 * d, d, b.dres_t, d, W(c, g.wproj(l)), d, EPI_GELU_BWD, b.dbig, 4 * d,
+              nullptr, nullptr, nullptr, b.fc[l]));
+    STEP(colsum(c, b.dbig, 4 * d, G + g.bfc(l), acc));
+    STEP(gemm_dw(c, d, 4 * d, b.ln2[l], b.dbig, G + g.wfc(l), acc));
+    STEP(gemm(c, 1, 1, M, d, 4 * d, b.dbig, 4 * d, W(c, g.wfc(l)), 4 * d, EPI_F32, b.dtmp, d));
+    STEP(ln_backward(c, b.resid_mid[l], b.ln2_mean[l], b.ln2_rstd[l], g.ln2g(l), g.ln2b(l),
+                     G + g.bo(l), 1, acc));
+    // h_mid = h_l + att W_o + b_o ; dres holds dh_mid
+    STEP(gemm_dw(c, d, d, b.att[l], b.dres_t, G + g.wo(l), acc));
+    STEP(gemm(c, 1, 1, M, d, d, b.dres_t, d, W(c, g.wo(l)), d, EPI_STORE, b.datt, d));
+    HIPCHK(launch_attn_bwd(g.bf16, g.B, g.T, g.H, g.hd, b.qkv[l], b.att[l], b.lse[l], b.datt,
+                           b.dqkv, b.dsum, c->stream));
+    STEP(colsum(c, b.dqkv, 3 * d, G + g.bqkv(l), acc));
+    STEP(gemm_dw(c, d, 3 * d, b.ln1[l], b.dqkv, G + g.wqkv(l), acc));
+    STEP(gemm(c, 1, 1, M, d, 3 * d, b.dqkv, 3 * d, W(c, g.wqkv(l)), 3 * d, EPI_F32, b.dtmp, d));
+    STEP(ln_backward(c, b.resid[l], b.ln1_mean[l], b.ln1_rstd[l], g.ln1g(l), g.ln1b(l),
+                     l > 0 ? G + g.bproj(l - 1) : nullptr, 1, acc));
+  }
+  HIPCHK(launch_embed_bwd(g.B, g.T, d, b.keys, b.dres, G + g.wte, G + g.wpe, acc, b.segpart,
+                          c->stream));
+  return GPT2_OK;
+}
+
+gpt2_status check_ctx(gpt2_ctx* c) {
+  if (!c) return fail(GPT2_E_INVALID, "context is NULL");
+  return GPT2_OK;
+}
+
+}  // namespace
+
+// ================================================================================== C ABI
+extern "C" {
+
+const char* gpt2_last_error(void) { return g_err.c_str(); }
+
+size_t gpt2_workspace_bytes(const gpt2_config* cfg) {
+  std::string why;
+  if (!validate(cfg, why) || !supported(cfg, why)) return 0;
+  Geo g = geometry(cfg);
+  Bufs b;
+  return carve(g, 0, b);
+}
+
+gpt2_status gpt2_param_count(const gpt2_config* cfg, size_t* n) {
+  std::string why;
+  if (!n) return fail(GPT2_E_INVALID, "n is NULL");
+  if (!validate(cfg, why)) return fail(GPT2_E_INVALID, why);
+  *n = (size_t)geometry(cfg).N;
+  return GPT2_OK;
+}
+
+gpt2_status gpt2_init(const gpt2_config* cfg, void* d_arena, size_t arena_bytes, void* hip_stream,
+                      gpt2_ctx** out) {
+  std::string why;
+  if (!out) return fail(GPT2_E_INVALID, "out is NULL");
+  *out = nullptr;
+  if (!validate(cfg, why)) return fail(GPT2_E_INVALID, why);
+  if (!supported(cfg, why)) return fail(GPT2_E_UNSUPPORTED, why);
+  if (!d_arena) return fail(GPT2_E_INVALID, "arena is NULL");
+  if (reinterpret_cast<uintptr_t>(d_arena) & 255)
+    return fail(GPT2_E_INVALID, "arena must be 256-byte aligned");
+  const size_t need = gpt2_workspace_bytes(cfg);
+  if (arena_bytes < need)
+    return fail(GPT2_E_NOMEM, "arena has " + std::to_string(arena_bytes) + " bytes, need " +
+                                  std::to_string(need));
+  gpt2_ctx* c = new gpt2_ctx();
+  c->cfg = *cfg;
+  c->g = geometry(cfg);
+  c->stream = static_cast<hipStream_t>(hip_stream);
+  carve(c->g, reinterpret_cast<uintptr_t>(d_arena), c->b);
+  c->segs = decay_segments(c->g);
+  const Geo& g = c->g;
+  Bufs& b = c->b;
+  auto bail = [&](gpt2_status s) { delete c; return s; };
+#define INITCHK(x)                                                                       \
+  do {                                                                                   \
+    hipError_t e_ = (x);                                                                 \
+    if (e_ != hipSuccess)                                                                \
+      return bail(fail(GPT2_E_HIP, std::string(#x) + " failed: " + hipGetErrorString(e_))); \
+  } while (0)
+  for (const Tensor& t : tensors(g)) {
+    if (t.matrix)
+      INITCHK(launch_init_normal(t.off, t.count, b.params + t.off, cfg->seed, cfg->init_std,
+                                 c->stream));
+    else
+      INITCHK(launch_fill(t.count, b.params + t.off, t.gain ? 1.0f : 0.0f, c->stream));
+  }
+  INITCHK(launch_fill(g.N, b.grads, 0.0f, c->stream));
+  INITCHK(launch_fill(g.N, b.m, 0.0f, c->stream));
+  INITCHK(launch_fill(g.N, b.v, 0.0f, c->stream));
+  if (g.bf16) INITCHK(launch_cast_bf16(g.N, b.params, b.shadow, c->stream));
+  INITCHK(hipMemsetAsync(b.err, 0, sizeof(int), c->stream));
+  INITCHK(hipMemsetAsync(b.loss, 0, sizeof(float), c->stream));
+  INITCHK(hipMemcpyAsync(b.segs, c->segs.data(), sizeof(AdamSeg) * c->segs.size(),
+                         hipMemcpyHostToDevice, c->stream));
+  INITCHK(hipStreamSynchronize(c->stream));
+#undef INITCHK
+  *out = c;
+  return GPT2_OK;
+}
+
+gpt2_status gpt2_forward_loss(gpt2_ctx* c, const int32_t* d_tokens, const int32_t* d_targets,
+                              float* d_loss) {
+  STEP(check_ctx(c));
+  if (!d_tokens || !d_targets) return fail(GPT2_E_INVALID, "tokens and targets must not be NULL");
+  STEP(forward(c, d_tokens, d_targets, d_loss));
+  c->have_forward = true;
+  return GPT2_OK;
+}
+
+gpt2_status gpt2_backward(gpt2_ctx* c, float grad_scale, int32_t accumulate) {
+  STEP(check_ctx(c));
+  if (!c->have_forward) return fail(GPT2_E_STATE, "backward needs a forward first");
+  if (accumulate != 0 && accumulate != 1) return fail(GPT2_E_INVALID, "accumulate must be 0 or 1");
+  if (!isfinite(grad_scale)) return fail(GPT2_E_INVALID, "grad_scale must be finite");
+  return backward(c, grad_scale, accumulate);
+}
+
+gpt2_status gpt2_adamw_step(gpt2_ctx* c, float lr, float beta1, float beta2, float eps,
+                            float weight_decay) {
+  STEP(check_ctx(c));
+  if (!(beta1 >= 0.0f && beta1 < 1.0f) || !(beta2 >= 0.0f && beta2 < 1.0f) || !(eps > 0.0f) ||
+      !isfinite(lr) || !isfinite(weight_decay))
+    return fail(GPT2_E_INVALID, "need 0 <= beta < 1, eps > 0, finite lr and weight_decay");
+  c->t += 1;
+  const double bc1 = 1.0 / (1.0 - pow((double)beta1, (double)c->t));
+  const double bc2 = 1.0 / (1.0 - pow((double)beta2, (double)c->t));
+  Timed t(c, FAM_ADAMW, 30.0 * c->g.N);
+  HIPCHK(launch_adamw(c->g.N, c->b.params, c->b.grads, c->b.m, c->b.v, c->b.shadow,
+                      c->b.segs, (int)c->segs.size(), lr, beta1, beta2, eps, weight_decay,
+                      (float)bc1, (float)bc2, c->stream));
+  return GPT2_OK;
+}
+
+gpt2_status gpt2_check(gpt2_ctx* c) {
+  STEP(check_ctx(c));
+  HIPCHK(hipStreamSynchronize(c->stream));
+  int err = 0;
+  HIPCHK(hipMemcpy(&err, c->b.err, sizeof(int), hipMemcpyDeviceToHost));
+  if (err) {
+    const int zero = 0;
+    HIPCHK(hipMemcpy(c->b.err, &zero, sizeof(int), hipMemcpyHostToDevice));
+    std::string what;
+    if (err & ERR_TOKEN_RANGE) what += "token id outside [0, vocab); ";
+    if (err & ERR_TARGET_RANGE) what += "target id outside [0, vocab); ";
+    return fail(GPT2_E_DEVICE, what);
+  }
+  return GPT2_OK;
+}
+
+gpt2_status gpt2_destroy(gpt2_ctx* c) {
+  if (!c) return fail(GPT2_E_INVALID, "context is NULL");
+  for (hipEvent_t e : c->ev) hipEventDestroy(e);
+  delete c;
+  return GPT2_OK;
+}
+
+static gpt2_status copy_flat(gpt2_ctx* c, int32_t set, float* dev, float* host, size_t n) {
+  if (!host) return fail(GPT2_E_INVALID, "host buffer is NULL");
+  if (n != (size_t)c->g.N) return fail(GPT2_E_INVALID, "n must equal the parameter count");
+  HIPCHK(hipStreamSynchronize(c->stream));
+  if (set)
+    HIPCHK(hipMemcpy(dev, host, n * sizeof(float), hipMemcpyHostToDevice));
+  else
+    HIPCHK(hipMemcpy(host, dev, n * sizeof(float), hipMemcpyDeviceToHost));
+  return GPT2_OK;
+}
+
+gpt2_status gpt2_copy_params(gpt2_ctx* c, int32_t set, float* host, size_t n) {
+  STEP(check_ctx(c));
+  STEP(copy_flat(c, set, c->b.params, host, n));
+  if (set && c->g.bf16) {
+    HIPCHK(launch_cast_bf16(c->g.N, c->b.params, c->b.shadow, c->stream));
+    HIPCHK(hipStreamSynchronize(c->stream));
+  }
+  return GPT2_OK;
+}
+
+gpt2_status gpt2_copy_grads(gpt2_ctx* c, int32_t set, float* host, size_t n) {
+  STEP(check_ctx(c));
+  return copy_flat(c, set, c->b.grads, host, n);
+}
+
+gpt2_status gpt2_copy_adam_state(gpt2_ctx* c, int32_t set, float* host_m, float* host_v, size_t n,
+                                 int64_t* host_t) {
+  STEP(check_ctx(c));
+  if (!host_t) return fail(GPT2_E_INVALID, "t is NULL");
+  STEP(copy_flat(c, set, c->b.m, host_m, n));
+  STEP(copy_flat(c, set, c->b.v, host_v, n));
+  if (set) {
+    if (*host_t < 0) return fail(GPT2_E_INVALID, "t must be >= 0");
+    c->t = *host_t;
+  } else {
+    *host_t = c->t;
+  }
+  return GPT2_OK;
+}
+
+gpt2_status gpt2_copy_row_loss(gpt2_ctx* c, float* host, size_t n) {
+  STEP(check_ctx(c));
+  if (!host) return fail(GPT2_E_INVALID, "host buffer is NULL");
+  if (n != (size_t)c->g.M) return fail(GPT2_E_INVALID, "n must equal batch * seq_len");
+  if (!c->have_forward) return fail(GPT2_E_STATE, "no forward has run");
+  HIPCHK(hipStreamSynchronize(c->stream));
+  HIPCHK(hipMemcpy(host, c->b.row_loss, n * sizeof(float), hipMemcpyDeviceToHost));
+  return GPT2_OK;
+}
+
+gpt2_status gpt2_timing_begin(gpt2_ctx* c, int32_t family) {
+  STEP(check_ctx(c));
+  if (family < 0 || family > 4) return fail(GPT2_E_INVALID, "family must be 0..4");
+  if (c->ev.empty()) {
+    c->ev.resize(2 * TIMING_CAP);
+    for (auto& e : c->ev) HIPCHK(hipEventCreate(&e));
+  }
+  c->timing_family = family;
+  c->timed = 0;
+  c->timed_work = 0.0;
+  return GPT2_OK;
+}
+
+gpt2_status gpt2_timing_end(gpt2_ctx* c, double* total_ms, int64_t* launches, double* work) {
+  STEP(check_ctx(c));
+  if (!total_ms || !launches || !work) return fail(GPT2_E_INVALID, "output pointer is NULL");
+  c->timing_family = -1;
+  HIPCHK(hipStreamSynchronize(c->stream));
+  double ms = 0.0;
+  for (int i = 0; i < c->timed; ++i) {
+    float e = 0.0f;
+    HIPCHK(hipEventElapsedTime(&e, c->ev[2 * i], c->ev[2 * i + 1]));
+    ms += e;
+  }
+  *total_ms = ms;
+  *launches = c->timed;
+  *work = c->timed_work;
+  return GPT2_OK;
+}
+
+gpt2_status gpt2_op_gemm(int32_t precision, int32_t a_kmajor, int32_t b_kmajor, int32_t m,
+                         int32_t n, int32_t k, const void* d_a, int64_t lda, const void* d_b,
+                         int64_t ldb, float* d_c, int64_t ldc, float alpha, float beta,
+                         void* hip_stream) {
+  if (precision != GPT2_FP32 && precision != GPT2_BF16) return fail(GPT2_E_INVALID, "precision");
+  if (m < 0 || n < 0 || k < 0) return fail(GPT2_E_INVALID, "negative size");
+  if (!d_a || !d_b || !d_c) return fail(GPT2_E_INVALID, "NULL operand");
+  const int a_row = a_kmajor ? k : m, b_row = b_kmajor ? k : n;
+  if (lda < a_row || ldb < b_row || ldc < n) return fail(GPT2_E_INVALID, "leading dimension too small");
+  if (a_row % 8 || b_row % 8 || lda % 8 || ldb % 8)
+    return fail(GPT2_E_UNSUPPORTED, "stored row lengths and leading dimensions must be multiples of 8");
+  GemmParams p{};
+  p.A = d_a; p.lda = lda; p.B = d_b; p.ldb = ldb; p.M = m; p.N = n; p.K = k; p.k_split = k;
+  p.epi = EPI_F32; p.C = d_c; p.ldc = ldc; p.alpha = alpha; p.beta = beta;
+  const bool bf = precision == GPT2_BF16;
+  int tile = TILE_128;
+  if (bf) {
+    const int64_t t256 = (int64_t)((m + 255) / 256) * ((n + 255) / 256);
+    const int64_t t2 = (int64_t)((m + 255) / 256) * ((n + 127) / 128);
+    tile = t256 >= 512 ? TILE_256 : (t2 >= 256 ? TILE_256x128 : TILE_128);
+  }
+  HIPCHK(launch_gemm(bf, a_kmajor ? 1 : 0, b_kmajor ? 1 : 0, tile, 1, 0, p,
+                     static_cast<hipStream_t>(hip_stream)));
+  return GPT2_OK;
+}
+
+static gpt2_status attn_args(int32_t precision, int32_t batch, int32_t seq_len, int32_t n_head,
+                             int32_t head_dim) {
+  if (precision != GPT2_FP32 && precision != GPT2_BF16) return fail(GPT2_E_INVALID, "precision");
+  if (batch < 0 || seq_len < 0 || n_head < 1) return fail(GPT2_E_INVALID, "bad sizes");
+  if (head_dim != 16 && head_dim != 32 && head_dim != 64)
+    return fail(GPT2_E_UNSUPPORTED, "head_dim must be 16, 32 or 64");
+  return GPT2_OK;
+}
+
+gpt2_status gpt2_op_attention_forward(int32_t precision, int32_t batch, int32_t seq_len,
+                                      int32_t n_head, int32_t head_dim, const void* d_qkv,
+                                      void* d_out, float* d_lse, void* hip_stream) {
+  STEP(attn_args(precision, batch, seq_len, n_head, head_dim));
+  if (!d_qkv || !d_out || !d_lse) return fail(GPT2_E_INVALID, "NULL buffer");
+  HIPCHK(launch_attn_fwd(precision == GPT2_BF16, batch, seq_len, n_head, head_dim, d_qkv, d_out,
+                         d_lse, static_cast<hipStream_t>(hip_stream)));
+  return GPT2_OK;
+}
+
+gpt2_status gpt2_op_attention_backward(int32_t precision, int32_t batch, int32_t seq_len,
+                                       int32_t n_head, int32_t head_dim, const void* d_qkv,
+                                       const void* d_out, const float* d_lse, const void* d_dout,
+                                       void* d_dqkv, float* d_scratch, void* hip_stream) {
+  STEP(attn_args(precision, batch, seq_len, n_head, head_dim));
+  if (!d_qkv || !d_out || !d_lse || !d_dout || !d_dqkv || !d_scratch)
+    return fail(GPT2_E_INVALID, "NULL buffer");
+  HIPCHK(launch_attn_bwd(precision == GPT2_BF16, batch, seq_len, n_head, head_dim, d_qkv, d_out,
+                         d_lse, d_dout, d_dqkv, d_scratch, static_cast<hipStream_t>(hip_stream)));
+  return GPT2_OK;
+}
+
+}  // extern "C"

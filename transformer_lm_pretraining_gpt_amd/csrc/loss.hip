@@ -1,0 +1,133 @@
+// Fused softmax cross-entropy over the padded vocabulary (HBM-bound).
+//
+// The loss is the cross-entropy of the next token ("Pré-treinar um LLM", opening paragraph on the
+// objective). Logits have vocab_padded columns (50257 padded to 50304, "Criei GPT-2 do zero com
+// uma RTX 4090", section "Configuração do treinamento"); the padded columns are masked out: they
+// take no part in the log-sum-exp and receive zero gradient.
+//
+// One block per row reads the row once into registers (16-byte vectors), forms the max, the sum
+// of exponentials and the log-sum-exp, writes the per-row loss lse - z[y], and overwrites the row
+// in place with softmax(z) - onehot(y) (zeros in the padded columns). The 1/M mean and the
+// backward's grad_scale are applied later, as the alpha of the LM-head gradient products, so no
+// probability matrix is ever written besides this in-place gradient.
+#include <math.h>
+
+#include "common.h"
+#include "kernels.h"
+
+namespace {
+
+constexpr int THREADS = 512;
+constexpr int MAXV = 16;  // 16-byte vectors per thread held in registers
+constexpr float LOG2E = 1.4426950408889634f;
+
+DEV float block_reduce(float v, float* sh, bool is_max) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  v = is_max ? wave_max(v) : wave_sum(v);
+  __syncthreads();
+  if (lane == 0) sh[wave] = v;
+  __syncthreads();
+  float r = sh[0];
+  for (int w = 1; w < THREADS / 64; ++w) r = is_max ? fmaxf(r, sh[w]) : r + sh[w];
+  return r;
+}
+
+template <typename T>
+__global__ __launch_bounds__(THREADS) void xent_kernel(int V, int Vp, T* __restrict__ logits,
+                                                       const int32_t* __restrict__ targets,
+                                                       float* __restrict__ row_loss,
+                                                       int* __restrict__ err) {
+  constexpr int VE = 16 / (int)sizeof(T);
+  __shared__ float sh[THREADS / 64];
+  const int row = blockIdx.x, tid = threadIdx.x;
+  T* z = logits + (int64_t)row * Vp;
+  const int nvec = Vp / VE;
+  int y = targets[row];
+  if (y < 0 || y >= V) {
+    if (tid == 0) atomicOr(err, ERR_TARGET_RANGE);
+    y = 0;  // keep the reads in bounds; the flagged result is not used
+  }
+  u32x4 reg[MAXV];
+  float mx = -INFINITY;
+#pragma unroll
+  for (int k = 0; k < MAXV; ++k) {
+    const int v = tid + k * THREADS;
+    if (v < nvec) {
+      reg[k] = ld16(z + v * VE);
+      float f[VE];
+      Vec<T>::unpack(reg[k], f);
+#pragma unroll
+      for (int e = 0; e < VE; ++e)
+        if (v * VE + e < V) mx = fmaxf(mx, f[e]);
+    }
+  }
+  mx = block_reduce(mx, sh, true);
+  float sum = 0.0f;
+#pragma unroll
+  for (int k = 0; k < MAXV; ++k) {
+    const int v = tid + k * THREADS;
+    if (v < nvec) {
+      float f[VE];
+      Vec<T>::unpack(reg[k], f);
+#pragma unroll
+      for (int e = 0; e < VE; ++e)
+        if (v * VE + e < V) sum += exp2f((f[e] - mx) * LOG2E);
+    }
+  }
+  sum = block_reduce(sum, sh, false);
+  const float lse = mx + logf(sum);
+  if (tid == 0) row_loss[row] = lse - to_f32(z[y]);
+  __syncthreads();  // z[y] is read before any thread overwrites the row
+#pragma unroll
+  for (int k = 0; k < MAXV; ++k) {
+    const int v = tid + k * THREADS;
+    if (v < nvec) {
+      float f[VE];
+      Vec<T>::unpack(reg[k], f);
+#pragma unroll
+      for (int e = 0; e < VE; ++e) {
+        const int j = v * VE + e;
+        f[e] = j < V ? exp2f((f[e] - lse) * LOG2E) - (j == y ? 1.0f : 0.0f) : 0.0f;
+      }
+      st16(z + v * VE, Vec<T>::pack(f));
+    }
+  }
+}
+
+__global__ __launch_bounds__(256) void loss_mean_kernel(int M, const float* __restrict__ rows,
+                                                        float* __restrict__ out,
+                                                        float* __restrict__ out_user) {
+  __shared__ float sh[4];
+  float s = 0.0f;
+  for (int i = threadIdx.x; i < M; i += 256) s += rows[i];
+  s = wave_sum(s);
+  if ((threadIdx.x & 63) == 0) sh[threadIdx.x >> 6] = s;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    const float mean = (((sh[0] + sh[1]) + sh[2]) + sh[3]) / (float)M;
+    out[0] = mean;
+    if (out_user) out_user[0] = mean;
+  }
+}
+
+}  // namespace
+
+hipError_t launch_xent(bool is_bf16, int M, int V, int Vp, void* logits, const int32_t* targets,
+                       float* row_loss, int* err, hipStream_t s) {
+  if (M == 0) return hipSuccess;
+  const int ve = is_bf16 ? 8 : 4;
+  if (Vp % ve || Vp / ve > MAXV * THREADS) return hipErrorInvalidValue;
+  if (is_bf16)
+    hipLaunchKernelGGL(xent_kernel<bf16>, dim3(M), dim3(THREADS), 0, s, V, Vp,
+                       static_cast<bf16*>(logits), targets, row_loss, err);
+  else
+    hipLaunchKernelGGL(xent_kernel<float>, dim3(M), dim3(THREADS), 0, s, V, Vp,
+                       static_cast<float*>(logits), targets, row_loss, err);
+  return hipGetLastError();
+}
+
+hipError_t launch_loss_mean(int M, const float* row_loss, float* loss_out, float* loss_user,
+                            hipStream_t s) {
+  hipLaunchKernelGGL(loss_mean_kernel, dim3(1), dim3(256), 0, s, M, row_loss, loss_out, loss_user);
+  return hipGetLastError();
+}

@@ -1,0 +1,247 @@
+// LayerNorm forward / backward and deterministic column reductions (bias and LN-parameter
+// gradients). HBM-bound; one wave per row, fp32 statistics.
+//
+// LayerNorm of the pre-LN GPT-2 block (the block the nanoGPT-style code of "Criei GPT-2 do zero
+// com uma RTX 4090", section "Ambiente", builds): mean, biased variance, eps = 1e-5,
+//   y = (x - mean) * rstd * g + b,  rstd = 1 / sqrt(var + eps).
+// Backward, with xhat = (x - mean) * rstd and dxh = dy * g:
+//   dx = rstd * (dxh - mean(dxh) - xhat * mean(dxh * xhat)),  dg = sum_rows dy * xhat,
+//   db = sum_rows dy.
+// Column sums never use atomics: each block writes its partial row, a second kernel adds the
+// partials in a fixed order, so results are bitwise reproducible.
+#include "common.h"
+#include "kernels.h"
+
+namespace {
+
+constexpr int MAXV = 8;  // float4 vectors per lane: d <= 2048
+constexpr float LN_EPS = 1e-5f;
+
+template <typename T>
+DEV void store4(T* dst, const float (&v)[4]) {
+  if constexpr (sizeof(T) == 2)
+    st8(dst, u32x2{pack_bf16(v[0], v[1]), pack_bf16(v[2], v[3])});
+  else
+    st16(dst, u32x4{__builtin_bit_cast(uint32_t, v[0]), __builtin_bit_cast(uint32_t, v[1]),
+                    __builtin_bit_cast(uint32_t, v[2]), __builtin_bit_cast(uint32_t, v[3])});
+}
+
+template <typename T>
+__global__ __launch_bounds__(256) void ln_fwd_kernel(int M, int d, const float* __restrict__ x,
+                                                     const float* __restrict__ g,
+                                                     const float* __restrict__ b,
+                                                     T* __restrict__ y, float* __restrict__ mean,
+                                                     float* __restrict__ rstd) {
+  const int lane = threadIdx.x & 63;
+  const int row = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (row >= M) return;
+  const int nv = d >> 2;
+  const float* xr = x + (int64_t)row * d;
+  f32x4 xv[MAXV];
+  float s = 0.0f;
+#pragma unroll
+  for (int k = 0; k < MAXV; ++k) {
+    const int v = lane + 64 * k;
+    xv[k] = v < nv ? *reinterpret_cast<const f32x4*>(xr + 4 * v) : f32x4{0, 0, 0, 0};
+    s += (xv[k][0] + xv[k][1]) + (xv[k][2] + xv[k][3]);
+  }
+  const float mu = wave_sum(s) / (float)d;
+  float s2 = 0.0f;
+#pragma unroll
+  for (int k = 0; k < MAXV; ++k) {
+    const int v = lane + 64 * k;
+    if (v < nv) {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const float c = xv[k][e] - mu;
+        s2 += c * c;
+      }
+    }
+  }
+  const float var = wave_sum(s2) / (float)d;
+  const float r = 1.0f / sqrtf(var + LN_EPS);
+#pragma unroll
+  for (int k = 0; k < MAXV; ++k) {
+    const int v = lane + 64 * k;
+    if (v < nv) {
+      const f32x4 gv = *reinterpret_cast<const f32x4*>(g + 4 * v);
+      const f32x4 bv = *reinterpret_cast<const f32x4*>(b + 4 * v);
+      float o[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) o[e] = (xv[k][e] - mu) * r * gv[e] + bv[e];
+      store4<T>(y + (int64_t)row * d + 4 * v, o);
+    }
+  }
+  if (lane == 0) {
+    mean[row] = mu;
+    rstd[row] = r;
+  }
+}
+
+// One block = 4 waves over rows [blk*rpb, blk*rpb + rpb); wave w takes rows w, w+4, ...
+template <typename T>
+__global__ __launch_bounds__(256) void ln_bwd_kernel(
+    int M, int d, const float* __restrict__ dy, const float* __restrict__ x,
+    const float* __restrict__ mean, const float* __restrict__ rstd, const float* __restrict__ g,
+    float* __restrict__ dres, int has_dres, T* __restrict__ dres_t, float* __restrict__ part,
+    int rpb) {
+  extern __shared__ float red[];  // [4][d]
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int nv = d >> 2;
+  f32x4 pg[MAXV], pb[MAXV], pr[MAXV], gv[MAXV];
+#pragma unroll
+  for (int k = 0; k < MAXV; ++k) {
+    pg[k] = pb[k] = pr[k] = f32x4{0, 0, 0, 0};
+    const int v = lane + 64 * k;
+    gv[k] = v < nv ? *reinterpret_cast<const f32x4*>(g + 4 * v) : f32x4{0, 0, 0, 0};
+  }
+  const int r0 = blockIdx.x * rpb, r1 = min(M, r0 + rpb);
+  for (int row = r0 + wave; row < r1; row += 4) {
+    const float mu = mean[row], rs = rstd[row];
+    const int64_t base = (int64_t)row * d;
+    f32x4 xh[MAXV], dyv[MAXV];
+    float s1 = 0.0f, s2 = 0.0f;
+#pragma unroll
+    for (int k = 0; k < MAXV; ++k) {
+      const int v = lane + 64 * k;
+      if (v < nv) {
+        const f32x4 xv = *reinterpret_cast<const f32x4*>(x + base + 4 * v);
+        dyv[k] = *reinterpret_cast<const f32x4*>(dy + base + 4 * v);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          xh[k][e] = (xv[e] - mu) * rs;
+          const float dxh = dyv[k][e] * gv[k][e];
+          s1 += dxh;
+          s2 += dxh * xh[k][e];
+        }
+      }
+    }
+    s1 = wave_sum(s1) / (float)d;
+    s2 = wave_sum(s2) / (float)d;
+#pragma unroll
+    for (int k = 0; k < MAXV; ++k) {
+      const int v = lane + 64 * k;
+      if (v < nv) {
+        f32x4 nw = has_dres ? *reinterpret_cast<const f32x4*>(dres + base + 4 * v)
+                            : f32x4{0, 0, 0, 0};
+        float o[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const float dxh = dyv[k][e] * gv[k][e];
+          nw[e] += rs * (dxh - s1 - xh[k][e] * s2);
+          o[e] = nw[e];
+          pg[k][e] += dyv[k][e] * xh[k][e];
+          pb[k][e] += dyv[k][e];
+          pr[k][e] += nw[e];
+        }
+        *reinterpret_cast<f32x4*>(dres + base + 4 * v) = nw;
+        store4<T>(dres_t + base + 4 * v, o);
+      }
+    }
+  }
+  // combine the 4 waves in a fixed order, one partial kind at a time
+  float* out = part + (int64_t)blockIdx.x * 3 * d;
+#pragma unroll
+  for (int kind = 0; kind < 3; ++kind) {
+#pragma unroll
+    for (int k = 0; k < MAXV; ++k) {
+      const int v = lane + 64 * k;
+      if (v < nv)
+        *reinterpret_cast<f32x4*>(red + wave * d + 4 * v) =
+            kind == 0 ? pg[k] : (kind == 1 ? pb[k] : pr[k]);
+    }
+    __syncthreads();
+    for (int j = threadIdx.x; j < d; j += 256)
+      out[kind * d + j] = ((red[j] + red[d + j]) + red[2 * d + j]) + red[3 * d + j];
+    __syncthreads();
+  }
+}
+
+template <typename T>
+__global__ __launch_bounds__(256) void colsum_partial_kernel(int M, int N,
+                                                             const T* __restrict__ src,
+                                                             int64_t ld, float* __restrict__ part,
+                                                             int rpb) {
+  constexpr int VE = 16 / (int)sizeof(T);
+  const int nvec = N / VE;
+  const int r0 = blockIdx.x * rpb, r1 = min(M, r0 + rpb);
+  for (int cv = threadIdx.x; cv < nvec; cv += 256) {
+    float acc[VE];
+#pragma unroll
+    for (int e = 0; e < VE; ++e) acc[e] = 0.0f;
+    for (int row = r0; row < r1; ++row) {
+      float f[VE];
+      Vec<T>::unpack(ld16(src + (int64_t)row * ld + cv * VE), f);
+#pragma unroll
+      for (int e = 0; e < VE; ++e) acc[e] += f[e];
+    }
+    float* out = part + (int64_t)blockIdx.x * N + cv * VE;
+#pragma unroll
+    for (int e = 0; e < VE; ++e) out[e] = acc[e];
+  }
+}
+
+__global__ void colsum_reduce_kernel(const float* __restrict__ part, int nparts, int64_t stride,
+                                     int n, float* __restrict__ out, int accumulate) {
+  const int j = blockIdx.x * blockDim.x + threadIdx.x;
+  if (j >= n) return;
+  float s = 0.0f;
+  for (int p = 0; p < nparts; ++p) s += part[(int64_t)p * stride + j];
+  out[j] = accumulate ? out[j] + s : s;
+}
+
+}  // namespace
+
+hipError_t launch_ln_fwd(bool is_bf16, int M, int d, const float* x, const float* g,
+                         const float* b, void* y, float* mean, float* rstd, hipStream_t s) {
+  if (M == 0) return hipSuccess;
+  if (d % 4 || d > 4 * 64 * MAXV) return hipErrorInvalidValue;
+  dim3 grid((M + 3) / 4);
+  if (is_bf16)
+    hipLaunchKernelGGL(ln_fwd_kernel<bf16>, grid, dim3(256), 0, s, M, d, x, g, b,
+                       static_cast<bf16*>(y), mean, rstd);
+  else
+    hipLaunchKernelGGL(ln_fwd_kernel<float>, grid, dim3(256), 0, s, M, d, x, g, b,
+                       static_cast<float*>(y), mean, rstd);
+  return hipGetLastError();
+}
+
+int ln_bwd_blocks(int M, int rows_per_block) { return (M + rows_per_block - 1) / rows_per_block; }
+
+hipError_t launch_ln_bwd(bool is_bf16, int M, int d, const float* dy, const float* x,
+                         const float* mean, const float* rstd, const float* g, float* dres,
+                         int has_dres, void* dres_t, float* part, int rows_per_block,
+                         hipStream_t s) {
+  if (M == 0) return hipSuccess;
+  if (d % 4 || d > 4 * 64 * MAXV) return hipErrorInvalidValue;
+  dim3 grid(ln_bwd_blocks(M, rows_per_block));
+  const size_t lds = 4 * (size_t)d * sizeof(float);
+  if (is_bf16)
+    hipLaunchKernelGGL(ln_bwd_kernel<bf16>, grid, dim3(256), lds, s, M, d, dy, x, mean, rstd, g,
+                       dres, has_dres, static_cast<bf16*>(dres_t), part, rows_per_block);
+  else
+    hipLaunchKernelGGL(ln_bwd_kernel<float>, grid, dim3(256), lds, s, M, d, dy, x, mean, rstd, g,
+                       dres, has_dres, static_cast<float*>(dres_t), part, rows_per_block);
+  return hipGetLastError();
+}
+
+hipError_t launch_colsum_partial(bool src_bf16, int M, int N, const void* src, int64_t ld,
+                                 float* part, int rows_per_block, hipStream_t s) {
+  if (M == 0) return hipSuccess;
+  dim3 grid((M + rows_per_block - 1) / rows_per_block);
+  if (src_bf16)
+    hipLaunchKernelGGL(colsum_partial_kernel<bf16>, grid, dim3(256), 0, s, M, N,
+                       static_cast<const bf16*>(src), ld, part, rows_per_block);
+  else
+    hipLaunchKernelGGL(colsum_partial_kernel<float>, grid, dim3(256), 0, s, M, N,
+                       static_cast<const float*>(src), ld, part, rows_per_block);
+  return hipGetLastError();
+}
+
+hipError_t launch_colsum_reduce(const float* part, int nparts, int64_t stride, int n, float* out,
+                                int accumulate, hipStream_t s) {
+  if (n == 0) return hipSuccess;
+  hipLaunchKernelGGL(colsum_reduce_kernel, dim3((n + 255) / 256), dim3(256), 0, s, part, nparts,
+                     stride, n, out, accumulate);
+  return hipGetLastError();
+}

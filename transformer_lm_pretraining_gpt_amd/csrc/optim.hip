@@ -1,0 +1,173 @@
+// AdamW update, parameter initialisation and the bf16 weight copy (all HBM-bound, flat over N).
+//
+// AdamW keeps two moments per parameter ("Pré-treinar um LLM", paragraph on memory: weight,
+// gradient, m and v in fp32) and is the optimiser of the pretraining objective (same page,
+// opening paragraph). Per element, with the bias corrections bc1 = 1 / (1 - b1^t) and
+// bc2 = 1 / (1 - b2^t) computed on the host in double precision:
+//   m = b1 m + (1 - b1) g;  v = b2 v + (1 - b2) g^2;
+//   p = p - lr * ( m bc1 / (sqrt(v bc2) + eps) + wd p ),  wd applied to 2-D tensors only.
+// One pass reads p, g, m, v (16 B) and writes p, m, v (12 B) plus the bf16 copy (2 B) that the
+// matrix products read (the half-precision weights of the ZeRO accounting, same page).
+//
+// Initialisation draws N(0, std^2) with Philox4x32-10 (Salmon, Moraes, Dror, Shaw, "Parallel
+// random numbers: as easy as 1, 2, 3", SC 2011) as a counter-based generator: element i takes
+// output word i%4 of block i/4, keyed by the seed, through the Box-Muller transform.
+#include <math.h>
+
+#include "common.h"
+#include "kernels.h"
+
+namespace {
+
+constexpr int THREADS = 256;
+
+__global__ __launch_bounds__(THREADS) void adamw_kernel(int64_t n4, float* __restrict__ p,
+                                                        const float* __restrict__ g,
+                                                        float* __restrict__ m,
+                                                        float* __restrict__ v,
+                                                        bf16* __restrict__ shadow,
+                                                        const AdamSeg* __restrict__ segs,
+                                                        int nseg, float lr, float b1, float b2,
+                                                        float eps, float wd, float bc1,
+                                                        float bc2) {
+  for (int64_t i = (int64_t)blockIdx.x * THREADS + threadIdx.x; i < n4;
+       i += (int64_t)gridDim.x * THREADS) {
+    const int64_t e = 4 * i;
+    // segment holding element e (segments are sorted, the first begins at 0)
+    int lo = 0, hi = nseg - 1;
+    while (lo < hi) {
+      const int mid = (lo + hi + 1) >> 1;
+      if (segs[mid].begin <= e) lo = mid; else hi = mid - 1;
+    }
+    const float wdi = segs[lo].decay ? wd : 0.0f;
+    f32x4 pv = *reinterpret_cast<const f32x4*>(p + e);
+    const f32x4 gv = *reinterpret_cast<const f32x4*>(g + e);
+    f32x4 mv = *reinterpret_cast<const f32x4*>(m + e);
+    f32x4 vv = *reinterpret_cast<const f32x4*>(v + e);
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      mv[k] = b1 * mv[k] + (1.0f - b1) * gv[k];
+      vv[k] = b2 * vv[k] + (1.0f - b2) * gv[k] * gv[k];
+      const float upd = (mv[k] * bc1) / (sqrtf(vv[k] * bc2) + eps);
+      pv[k] = pv[k] - lr * (upd + wdi * pv[k]);
+    }
+    *reinterpret_cast<f32x4*>(p + e) = pv;
+    *reinterpret_cast<f32x4*>(m + e) = mv;
+    *reinterpret_cast<f32x4*>(v + e) = vv;
+    if (shadow) st8(shadow + e, u32x2{pack_bf16(pv[0], pv[1]), pack_bf16(pv[2], pv[3])});
+  }
+}
+
+DEV void mulhilo(uint32_t a, uint32_t b, uint32_t& hi, uint32_t& lo) {
+  const uint64_t r = (uint64_t)a * b;
+  hi = (uint32_t)(r >> 32);
+  lo = (uint32_t)r;
+}
+
+DEV u32x4 philox4x32_10(u32x4 c, uint32_t k0, uint32_t k1) {
+  for (int round = 0; round < 10; ++round) {
+    uint32_t hi0, lo0, hi1, lo1;
+    mulhilo(0xD2511F53u, c[0], hi0, lo0);
+    mulhilo(0xCD9E8D57u, c[2], hi1, lo1);
+    c = u32x4{hi1 ^ c[1] ^ k0, lo1, hi0 ^ c[3] ^ k1, lo0};
+    k0 += 0x9E3779B9u;
+    k1 += 0xBB67AE85u;
+  }
+  return c;
+}
+
+// uniform in (0, 1]
+DEV float u01(uint32_t x) { return ((float)(x >> 8) + 1.0f) * (1.0f / 16777216.0f); }
+
+__global__ __launch_bounds__(THREADS) void init_normal_kernel(int64_t begin, int64_t count,
+                                                              float* __restrict__ p,
+                                                              uint64_t seed, float stdv) {
+  const int64_t n4 = (count + 3) / 4;
+  for (int64_t i = (int64_t)blockIdx.x * THREADS + threadIdx.x; i < n4;
+       i += (int64_t)gridDim.x * THREADS) {
+    const int64_t gi = begin + 4 * i;  // global element index drives the counter
+    const int64_t blk = gi >> 2;
+    const u32x4 r = philox4x32_10(u32x4{(uint32_t)blk, (uint32_t)(blk >> 32), 0u, 0u},
+                                  (uint32_t)seed, (uint32_t)(seed >> 32));
+    float z[4];
+    for (int pr = 0; pr < 2; ++pr) {
+      const float u1 = u01(r[2 * pr]), u2 = u01(r[2 * pr + 1]);
+      const float rad = sqrtf(-2.0f * logf(u1));
+      const float ang = 6.283185307179586f * u2;
+      z[2 * pr] = rad * cosf(ang);
+      z[2 * pr + 1] = rad * sinf(ang);
+    }
+    // begin may not be a multiple of 4: element gi + k uses word (gi + k) % 4 of its own block
+    for (int k = 0; k < 4; ++k) {
+      const int64_t j = 4 * i + k;
+      if (j >= count) break;
+      const int64_t ge = begin + j;
+      float val;
+      if ((ge >> 2) == blk) {
+        val = z[ge & 3];
+      } else {
+        const u32x4 r2 = philox4x32_10(u32x4{(uint32_t)(ge >> 2), (uint32_t)(ge >> 34), 0u, 0u},
+                                       (uint32_t)seed, (uint32_t)(seed >> 32));
+        const int w = (int)(ge & 3), pr = w >> 1;
+        const float u1 = u01(r2[2 * pr]), u2 = u01(r2[2 * pr + 1]);
+        const float rad = sqrtf(-2.0f * logf(u1));
+        const float ang = 6.283185307179586f * u2;
+        val = (w & 1) ? rad * sinf(ang) : rad * cosf(ang);
+      }
+      p[j] = stdv * val;
+    }
+  }
+}
+
+__global__ __launch_bounds__(THREADS) void fill_kernel(int64_t count, float* __restrict__ p,
+                                                       float value) {
+  for (int64_t i = (int64_t)blockIdx.x * THREADS + threadIdx.x; i < count;
+       i += (int64_t)gridDim.x * THREADS)
+    p[i] = value;
+}
+
+__global__ __launch_bounds__(THREADS) void cast_bf16_kernel(int64_t count,
+                                                            const float* __restrict__ src,
+                                                            bf16* __restrict__ dst) {
+  for (int64_t i = (int64_t)blockIdx.x * THREADS + threadIdx.x; i < count;
+       i += (int64_t)gridDim.x * THREADS)
+    dst[i] = (bf16)src[i];
+}
+
+unsigned grid_for(int64_t work) {
+  const int64_t g = (work + THREADS - 1) / THREADS;
+  return (unsigned)(g < 1 ? 1 : (g > 8192 ? 8192 : g));
+}
+
+}  // namespace
+
+hipError_t launch_adamw(int64_t n, float* p, const float* g, float* m, float* v, void* shadow,
+                        const AdamSeg* segs, int nseg, float lr, float b1, float b2, float eps,
+                        float wd, float bc1, float bc2, hipStream_t s) {
+  if (n % 4) return hipErrorInvalidValue;
+  const int64_t n4 = n / 4;
+  hipLaunchKernelGGL(adamw_kernel, dim3(grid_for(n4)), dim3(THREADS), 0, s, n4, p, g, m, v,
+                     static_cast<bf16*>(shadow), segs, nseg, lr, b1, b2, eps, wd, bc1, bc2);
+  return hipGetLastError();
+}
+
+hipError_t launch_init_normal(int64_t begin, int64_t count, float* p, uint64_t seed, float stdv,
+                              hipStream_t s) {
+  if (count <= 0) return hipSuccess;
+  hipLaunchKernelGGL(init_normal_kernel, dim3(grid_for((count + 3) / 4)), dim3(THREADS), 0, s,
+                     begin, count, p, seed, stdv);
+  return hipGetLastError();
+}
+
+hipError_t launch_fill(int64_t count, float* p, float value, hipStream_t s) {
+  if (count <= 0) return hipSuccess;
+  hipLaunchKernelGGL(fill_kernel, dim3(grid_for(count)), dim3(THREADS), 0, s, count, p, value);
+  return hipGetLastError();
+}
+
+hipError_t launch_cast_bf16(int64_t count, const float* src, void* dst, hipStream_t s) {
+  if (count <= 0) return hipSuccess;
+  hipLaunchKernelGGL(cast_bf16_kernel, dim3(grid_for(count)), dim3(THREADS), 0, s, count, src,
+                     static_cast<bf16*>(dst));
+  return hipGetLastError();
+}
