@@ -139,21 +139,20 @@ std::vector<AdamSeg> decay_segments(const Geo& g) {
 }
 
 // ------------------------------------------------------------------------------ GEMM plans
+// Tile choice measured on the GPT-2 shapes: 256x256 tiles only when they still give at least two
+// rounds of blocks over the 256 CUs; otherwise 128x128 tiles (several blocks per CU).
 int pick_tile(const Geo& g, int M, int N) {
   if (!g.bf16) return TILE_128;
-  const int64_t t256 = (int64_t)((M + 255) / 256) * ((N + 255) / 256);
-  const int64_t t256x128 = (int64_t)((M + 255) / 256) * ((N + 127) / 128);
-  if (t256 >= 512) return TILE_256;
-  if (t256x128 >= 256) return TILE_256x128;
-  return TILE_128;
+  return gemm_pick_tile(M, N);
 }
 
-// Split of the K = rows reduction of a weight gradient (in x out): enough blocks for 256 CUs.
+// Split of the K = rows reduction of a weight gradient (in x out): about four 128x128 blocks per
+// CU in flight; the fp32 partials are summed by a second kernel in a fixed order.
 struct Split { int splits, k_split; };
 Split pick_split(const Geo& g, int in, int out) {
-  const int kt = gemm_k_tile(g.bf16);
+  const int kt = 64;
   const int64_t tiles = (int64_t)((in + 127) / 128) * ((out + 127) / 128);
-  int s = (int)((512 + tiles - 1) / tiles);
+  int s = (int)((1024 + tiles - 1) / tiles);
   if (s < 1) s = 1;
   if (s > 8) s = 8;
   int per = (g.M + s - 1) / s;
@@ -363,14 +362,8 @@ gpt2_status ln_backward(gpt2_ctx* c, const float* x, const float* mean, const fl
   const int nblk = ln_bwd_blocks(g.M, LN_ROWS_PER_BLOCK);
   HIPCHK(launch_ln_bwd(g.bf16, g.M, g.d, c->b.dtmp, x, mean, rstd, c->b.params + g_off, c->b.dres,
                        has_dres, c->b.dres_t, c->b.colpart, LN_ROWS_PER_BLOCK, c->stream));
-  const int64_t stride = 3 * (int64_t)g.d;
-  HIPCHK(launch_colsum_reduce(c->b.colpart, nblk, stride, g.d, c->b.grads + g_off, accumulate,
-                              c->stream));
-  HIPCHK(launch_colsum_reduce(c->b.colpart + g.d, nblk, stride, g.d, c->b.grads + b_off,
-                              accumulate, c->stream));
-  if (bias_out)
-    HIPCHK(launch_colsum_reduce(c->b.colpart + 2 * g.d, nblk, stride, g.d, bias_out, accumulate,
-                                c->stream));
+  HIPCHK(launch_colsum_reduce3(c->b.colpart, nblk, 3 * (int64_t)g.d, g.d, c->b.grads + g_off,
+                               c->b.grads + b_off, bias_out, accumulate, c->stream));
   return GPT2_OK;
 }
 
@@ -695,12 +688,7 @@ gpt2_status gpt2_op_gemm(int32_t precision, int32_t a_kmajor, int32_t b_kmajor, 
   p.A = d_a; p.lda = lda; p.B = d_b; p.ldb = ldb; p.M = m; p.N = n; p.K = k; p.k_split = k;
   p.epi = EPI_F32; p.C = d_c; p.ldc = ldc; p.alpha = alpha; p.beta = beta;
   const bool bf = precision == GPT2_BF16;
-  int tile = TILE_128;
-  if (bf) {
-    const int64_t t256 = (int64_t)((m + 255) / 256) * ((n + 255) / 256);
-    const int64_t t2 = (int64_t)((m + 255) / 256) * ((n + 127) / 128);
-    tile = t256 >= 512 ? TILE_256 : (t2 >= 256 ? TILE_256x128 : TILE_128);
-  }
+  const int tile = bf ? gemm_pick_tile(m, n) : TILE_128;
   HIPCHK(launch_gemm(bf, a_kmajor ? 1 : 0, b_kmajor ? 1 : 0, tile, 1, 0, p,
                      static_cast<hipStream_t>(hip_stream)));
   return GPT2_OK;

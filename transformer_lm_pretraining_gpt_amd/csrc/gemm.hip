@@ -9,7 +9,7 @@
 //  * 256 threads = 4 waves in a 2 x 2 arrangement; block tile BM x BN, wave tile BM/2 x BN/2 made
 //    of 32 x 32 MFMA tiles (v_mfma_f32_32x32x16_bf16, or 4 x v_mfma_f32_32x32x2f32 for fp32).
 //  * K advances in 128-byte slabs (64 bf16 or 32 fp32). Each operand tile lives in LDS as rows of
-//    128 bytes, k contiguous, with the 16-byte chunk index XOR-swizzled by (row + row/8) mod 8 so
+//    128 bytes, k contiguous, with the 16-byte chunk index XOR-swizzled by (row/2) mod 8 so
 //    that both the fills and the MFMA fragment reads are free of bank conflicts.
 //  * Two LDS stages: the global loads of slab k+1 are issued before the MFMAs of slab k and land
 //    in registers; they are written to the other stage after the MFMAs; one barrier per slab.
@@ -26,7 +26,9 @@ namespace {
 constexpr int ROWB = 128;  // bytes of one k-slab row in LDS
 constexpr int THREADS = 256;
 
-DEV int swz(int row) { return (row + (row >> 3)) & 7; }
+// 16-byte chunk swizzle of a 128-byte LDS row: chosen by measurement (bank-conflict counter) to
+// make the 32-row fragment reads of the MFMA loop conflict-free on gfx950
+DEV int swz(int row) { return (row >> 1) & 7; }
 DEV int lds_off(int row, int chunk) { return row * ROWB + ((chunk ^ swz(row)) << 4); }
 
 DEV float gelu_tanh(float u) {
@@ -257,6 +259,272 @@ __global__ __launch_bounds__(THREADS) void gemm_kernel(GemmParams p) {
   }
 }
 
+// ------------------------------------------------------------------------------------------
+// bf16 product with direct global->LDS loads (global_load_lds_dwordx4), for K a multiple of 64.
+//
+// Each 16-byte load goes straight into LDS (no staging registers, no LDS write instructions),
+// so NSTAGE slabs can be in flight. K-major tiles use the XOR-swizzled 128-byte rows above.
+// Tiles stored k-row by k-row ([k][r], r contiguous) are copied as they are, with 16-byte chunk c
+// of k-row k placed at chunk c ^ 4(k mod 4); their MFMA fragments are read with
+// ds_read_b64_tr_b16, which hands each lane four consecutive k of one row: within a group of 16
+// lanes, lane i receives element i%4 of the 8-byte rows addressed by lanes i/4, 4+i/4, 8+i/4 and
+// 12+i/4, so lane j addressing k-row K0 + j/4 at column R0 + 4(j%4) gives lane i the values
+// (R0 + i, K0 .. K0+3). Rows beyond the matrix are loaded from the last valid row (in bounds;
+// their results are never stored).
+typedef __attribute__((address_space(3))) void lds_void_t;
+typedef __attribute__((ext_vector_type(4))) short s16x4;
+
+DEV void lds_dma16(const void* g, char* lds_wave_base) {
+  __builtin_amdgcn_global_load_lds(g, (lds_void_t*)lds_wave_base, 16, 0, 0);
+}
+DEV void wave_barrier_all() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+template <int N>
+DEV void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt");
+  // vmcnt in bits [3:0] and [15:14]; expcnt (7) and lgkmcnt (15) left unconstrained
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+  asm volatile("" ::: "memory");
+}
+DEV int tr_swz(int krow) { return (krow & 3) << 2; }
+
+// K-major LDS rows of RB bytes (RB = 128 or 64): chunk swizzle measured conflict-free on gfx950
+template <int RB>
+DEV int swz_rb(int row) {
+  if constexpr (RB == 128) return (row >> 1) & 7;
+  else return (row >> 2) & 3;
+}
+template <int RB>
+DEV int lds_off_rb(int row, int chunk) { return row * RB + ((chunk ^ swz_rb<RB>(row)) << 4); }
+
+template <int R, bool KMAJOR, int RB>
+struct DmaTile {
+  static constexpr int KT = RB / 2;                  // k per slab
+  static constexpr int PER_WAVE = R * RB / 4096;     // 1 KB wave-loads per slab per wave
+  // Issue this wave's loads of one slab (k0 .. k0+KT-1) into the stage buffer `dst`.
+  DEV static void issue(const bf16* __restrict__ base, int64_t ld, int r0, int r_total, int k0,
+                        char* dst, int wave, int lane) {
+#pragma unroll
+    for (int i = 0; i < PER_WAVE; ++i) {
+      const int q = wave * PER_WAVE + i;
+      const bf16* g;
+      if constexpr (KMAJOR) {
+        constexpr int CPR = RB / 16, RPI = 1024 / RB;  // chunks per row, rows per wave-load
+        const int row = RPI * q + lane / CPR;
+        const int c = (lane % CPR) ^ swz_rb<RB>(row);
+        const int r = min(r0 + row, r_total - 1);
+        g = base + (int64_t)r * ld + k0 + c * 8;
+      } else {
+        constexpr int CPR = R / 8;            // 16-byte chunks per k-row
+        constexpr int KPI = 1024 / (2 * R);   // k-rows per wave-load
+        const int krow = q * KPI + lane / CPR;
+        const int c = (lane % CPR) ^ tr_swz(krow);
+        int r = r0 + c * 8;
+        if (r >= r_total) r = r_total - 8;
+        g = base + (int64_t)(k0 + krow) * ld + r;
+      }
+      lds_dma16(g, dst + q * 1024);
+    }
+  }
+  // Fragment (32 rows from rw, k = 16s .. 16s+15 of the slab) for the calling lane.
+  DEV static u32x4 frag(const char* st, int rw, int s, int lane) {
+    if constexpr (KMAJOR) {
+      return *reinterpret_cast<const u32x4*>(st + lds_off_rb<RB>(rw + (lane & 31), 2 * s + (lane >> 5)));
+    } else {
+      const int g = lane >> 4, j = lane & 15;
+      const int r = rw + (g & 1) * 16 + 4 * (j & 3);
+      const int chunk = r >> 3, within = (r & 7) * 2;
+      u32x2 out[2];
+#pragma unroll
+      for (int t = 0; t < 2; ++t) {
+        const int krow = 16 * s + (g >> 1) * 8 + 4 * t + (j >> 2);
+        const char* a = st + krow * (2 * R) + ((chunk ^ tr_swz(krow)) << 4) + within;
+        const s16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (__attribute__((address_space(3))) s16x4*)(a));
+        out[t] = __builtin_bit_cast(u32x2, v);
+      }
+      return u32x4{out[0][0], out[0][1], out[1][0], out[1][1]};
+    }
+  }
+};
+
+template <int EPI, int MB, int NB>
+DEV void epilogue_rows(const f32x16 (&acc)[MB][NB], const GemmParams& p, float* buf, int row0,
+                       int col0, int lane) {
+  constexpr int WN = NB * 32;
+  constexpr int PITCH = WN + 4;  // floats; padding spreads the two lane halves over banks
+  constexpr int V4 = WN / 4;     // float4 per row
+  constexpr int RPP = 64 / V4;   // rows per pass
+  const int h = lane >> 5, l32 = lane & 31;
+  float* cf = static_cast<float*>(p.C);
+  if (EPI == EPI_F32) cf += (int64_t)blockIdx.z * p.c_split_stride;
+#pragma unroll
+  for (int i = 0; i < MB; ++i) {
+#pragma unroll
+    for (int j = 0; j < NB; ++j)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) buf[mfma_row(r, h) * PITCH + j * 32 + l32] = acc[i][j][r];
+    __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0): this wave's LDS writes are done
+    asm volatile("" ::: "memory");
+#pragma unroll
+    for (int pass = 0; pass < 32 / RPP; ++pass) {
+      const int rl = pass * RPP + lane / V4;
+      const int c4 = lane % V4;
+      const int row = row0 + i * 32 + rl;
+      const int col = col0 + c4 * 4;
+      const f32x4 v = *reinterpret_cast<const f32x4*>(buf + rl * PITCH + c4 * 4);
+      if (row < p.M && col < p.N) {
+        const int64_t o = (int64_t)row * p.ldc + col;
+        f32x4 bias = p.bias ? *reinterpret_cast<const f32x4*>(p.bias + col) : f32x4{0, 0, 0, 0};
+        float out[4];
+        if constexpr (EPI == EPI_STORE) {
+#pragma unroll
+          for (int e = 0; e < 4; ++e) out[e] = p.alpha * v[e] + bias[e];
+          st8(static_cast<bf16*>(p.C) + o, u32x2{pack_bf16(out[0], out[1]), pack_bf16(out[2], out[3])});
+        } else if constexpr (EPI == EPI_BIAS_GELU) {
+          float gl[4];
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            out[e] = v[e] + bias[e];
+            gl[e] = gelu_tanh(out[e]);
+          }
+          st8(static_cast<bf16*>(p.C) + o, u32x2{pack_bf16(out[0], out[1]), pack_bf16(out[2], out[3])});
+          st8(static_cast<bf16*>(p.C2) + o, u32x2{pack_bf16(gl[0], gl[1]), pack_bf16(gl[2], gl[3])});
+        } else if constexpr (EPI == EPI_BIAS_RESID) {
+          const f32x4 rs = *reinterpret_cast<const f32x4*>(p.resid + o);
+          *reinterpret_cast<f32x4*>(cf + o) = rs + v + bias;
+        } else if constexpr (EPI == EPI_GELU_BWD) {
+          const u32x2 u = ld8(static_cast<const bf16*>(p.aux) + o);
+          const float uf[4] = {bf16lo(u[0]), bf16hi(u[0]), bf16lo(u[1]), bf16hi(u[1])};
+#pragma unroll
+          for (int e = 0; e < 4; ++e) out[e] = v[e] * gelu_tanh_grad(uf[e]);
+          st8(static_cast<bf16*>(p.C) + o, u32x2{pack_bf16(out[0], out[1]), pack_bf16(out[2], out[3])});
+        } else {
+          f32x4 prev = f32x4{0, 0, 0, 0};
+          if (p.beta != 0.0f) prev = p.beta * *reinterpret_cast<const f32x4*>(cf + o);
+          *reinterpret_cast<f32x4*>(cf + o) = p.alpha * v + prev;
+        }
+      }
+    }
+    __builtin_amdgcn_s_waitcnt(0xc07f);
+    asm volatile("" ::: "memory");
+  }
+}
+
+template <int AK, int BKM, int BM, int BN, int RB, int NSTAGE, int MINB, int TAG>
+__global__ __launch_bounds__(THREADS, MINB) void gemm_dma_kernel(GemmParams p) {
+  constexpr int WM = BM / 2, WN = BN / 2;
+  constexpr int MB = WM / 32, NB = WN / 32;
+  constexpr int KT = RB / 2;
+  constexpr int KSTEPS = RB / 32;
+  constexpr int STAGE = (BM + BN) * RB;
+  using TA = DmaTile<BM, AK == 1, RB>;
+  using TB = DmaTile<BN, BKM == 1, RB>;
+  constexpr int LW = TA::PER_WAVE + TB::PER_WAVE;  // loads per wave per slab
+  __shared__ __attribute__((aligned(1024))) char smem[NSTAGE * STAGE];
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: LDS bases go to M0
+
+  const int tiles_m = (p.M + BM - 1) / BM, tiles_n = (p.N + BN - 1) / BN;
+  const int nblk = tiles_m * tiles_n;
+  int bid = blockIdx.x;
+  if ((nblk & 7) == 0) bid = (bid & 7) * (nblk >> 3) + (bid >> 3);
+  constexpr int GROUP = 8;
+  const int in_group = GROUP * tiles_n;
+  const int g = bid / in_group;
+  const int first_m = g * GROUP;
+  const int gsize = min(tiles_m - first_m, GROUP);
+  const int tm = first_m + (bid % in_group) % gsize;
+  const int tn = (bid % in_group) / gsize;
+  const int m0 = tm * BM, n0 = tn * BN;
+  const int k_begin = blockIdx.z * p.k_split;
+  const int k_end = min(p.K, k_begin + p.k_split);
+  const int nk = (k_end - k_begin) / KT;
+
+  const bf16* A = static_cast<const bf16*>(p.A);
+  const bf16* B = static_cast<const bf16*>(p.B);
+  const int wm0 = (wave >> 1) * WM, wn0 = (wave & 1) * WN;
+
+  f32x16 acc[MB][NB];
+#pragma unroll
+  for (int i = 0; i < MB; ++i)
+#pragma unroll
+    for (int j = 0; j < NB; ++j) acc[i][j] = f32x16{};
+
+#pragma unroll
+  for (int s = 0; s < NSTAGE - 1; ++s) {
+    if (s < nk) {
+      char* st = smem + s * STAGE;
+      TA::issue(A, p.lda, m0, p.M, k_begin + s * KT, st, wave, lane);
+      TB::issue(B, p.ldb, n0, p.N, k_begin + s * KT, st + BM * RB, wave, lane);
+    }
+  }
+  for (int kt = 0; kt < nk; ++kt) {
+    // slabs issued after kt: min(NSTAGE - 2, nk - 1 - kt)
+    const int after = min(NSTAGE - 2, nk - 1 - kt);
+    if constexpr (NSTAGE >= 4) {
+      if (after >= 2) wait_vmcnt<2 * LW>();
+      else if (after == 1) wait_vmcnt<LW>();
+      else wait_vmcnt<0>();
+    } else if constexpr (NSTAGE == 3) {
+      if (after >= 1) wait_vmcnt<LW>();
+      else wait_vmcnt<0>();
+    } else {
+      wait_vmcnt<0>();
+    }
+    wave_barrier_all();
+    const int nxt = kt + NSTAGE - 1;
+    if (nxt < nk) {
+      char* st = smem + (nxt % NSTAGE) * STAGE;
+      TA::issue(A, p.lda, m0, p.M, k_begin + nxt * KT, st, wave, lane);
+      TB::issue(B, p.ldb, n0, p.N, k_begin + nxt * KT, st + BM * RB, wave, lane);
+    }
+    const char* sa = smem + (kt % NSTAGE) * STAGE;
+    const char* sb = sa + BM * RB;
+    // fragments of k-step s+1 are read while the MFMAs of k-step s run
+    u32x4 fa[2][MB], fb[2][NB];
+#pragma unroll
+    for (int i = 0; i < MB; ++i) fa[0][i] = TA::frag(sa, wm0 + i * 32, 0, lane);
+#pragma unroll
+    for (int j = 0; j < NB; ++j) fb[0][j] = TB::frag(sb, wn0 + j * 32, 0, lane);
+#pragma unroll
+    for (int s = 0; s < KSTEPS; ++s) {
+      const int cur = s & 1;
+      if (s < KSTEPS - 1) {
+#pragma unroll
+        for (int i = 0; i < MB; ++i) fa[cur ^ 1][i] = TA::frag(sa, wm0 + i * 32, s + 1, lane);
+#pragma unroll
+        for (int j = 0; j < NB; ++j) fb[cur ^ 1][j] = TB::frag(sb, wn0 + j * 32, s + 1, lane);
+      }
+      // keep the reads of step s+1 ahead of the MFMAs of step s (the default scheduler would
+      // sink them to their use and expose the LDS latency every few MFMAs)
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int i = 0; i < MB; ++i)
+#pragma unroll
+        for (int j = 0; j < NB; ++j) Mfma<bf16>::mma(acc[i][j], fa[cur][i], fb[cur][j]);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  }
+
+  // all waves are done reading the stages: reuse the LDS for the epilogue
+  wait_vmcnt<0>();
+  wave_barrier_all();
+  float* buf = reinterpret_cast<float*>(smem) + wave * 32 * (WN + 4);
+  const int row0 = m0 + wm0, col0 = n0 + wn0;
+  switch (p.epi) {
+    case EPI_STORE: epilogue_rows<EPI_STORE, MB, NB>(acc, p, buf, row0, col0, lane); break;
+    case EPI_BIAS_GELU: epilogue_rows<EPI_BIAS_GELU, MB, NB>(acc, p, buf, row0, col0, lane); break;
+    case EPI_BIAS_RESID: epilogue_rows<EPI_BIAS_RESID, MB, NB>(acc, p, buf, row0, col0, lane); break;
+    case EPI_GELU_BWD: epilogue_rows<EPI_GELU_BWD, MB, NB>(acc, p, buf, row0, col0, lane); break;
+    default: epilogue_rows<EPI_F32, MB, NB>(acc, p, buf, row0, col0, lane); break;
+  }
+}
+
 __global__ void splitk_reduce_kernel(const float* __restrict__ part, int splits, int64_t stride,
                                      int M, int N, float* __restrict__ C, int64_t ldc, float alpha,
                                      float beta) {
@@ -270,8 +538,36 @@ __global__ void splitk_reduce_kernel(const float* __restrict__ part, int splits,
   C[src] = alpha * s + prev;
 }
 
+// Tile configurations of the direct-to-LDS kernel: 256x256 with 128-byte slabs, two stages
+// (128 KB LDS, one block per CU); 256x128 and 128x128 with 64-byte slabs, three stages (72 / 48 KB
+// LDS), two blocks per CU so that one block's epilogue overlaps the other's MFMAs.
+template <int AK, int BKM, int BM, int BN>
+hipError_t launch_dma(int splits, int tag, const GemmParams& p, hipStream_t s) {
+  constexpr int RB = (BM == 256 && BN == 256) ? 128 : 64;
+  constexpr int STAGE = (BM + BN) * RB;
+  constexpr int NSTAGE = (BM == 256 && BN == 256) ? 2 : 3;
+  constexpr int MINB = (BM == 256 && BN == 256) ? 1 : 2;
+  static_assert(NSTAGE * STAGE <= 160 * 1024, "LDS");
+  const int tiles = ((p.M + BM - 1) / BM) * ((p.N + BN - 1) / BN);
+  dim3 grid(tiles, 1, splits), block(THREADS);
+  if constexpr (AK == 1 && BKM == 1 && BM == 256 && BN == 256) {
+    if (tag == 1) {
+      hipLaunchKernelGGL((gemm_dma_kernel<AK, BKM, BM, BN, RB, NSTAGE, MINB, 1>), grid, block, 0, s, p);
+      return hipGetLastError();
+    }
+  }
+  hipLaunchKernelGGL((gemm_dma_kernel<AK, BKM, BM, BN, RB, NSTAGE, MINB, 0>), grid, block, 0, s, p);
+  return hipGetLastError();
+}
+
 template <typename T, int AK, int BKM, int BM, int BN>
 hipError_t launch_t(int splits, int tag, const GemmParams& p, hipStream_t s) {
+  if constexpr (sizeof(T) == 2) {
+    // direct-to-LDS pipeline when every slab is a whole 64-wide k-slab and rows fit the tiles
+    if (p.K % 64 == 0 && (splits == 1 || p.k_split % 64 == 0) && p.M >= (AK ? 1 : 8) &&
+        p.N >= (BKM ? 1 : 8))
+      return launch_dma<AK, BKM, BM, BN>(splits, tag, p, s);
+  }
   const int tiles = ((p.M + BM - 1) / BM) * ((p.N + BN - 1) / BN);
   dim3 grid(tiles, 1, splits), block(THREADS);
   // tag 1: a separately named copy of the LM-head product, so profilers report it on its own
@@ -312,6 +608,11 @@ hipError_t launch_type(int a_kmajor, int b_kmajor, int tile, int splits, int tag
 }  // namespace
 
 int gemm_k_tile(bool is_bf16) { return is_bf16 ? ROWB / 2 : ROWB / 4; }
+
+int gemm_pick_tile(int M, int N) {
+  const int64_t t256 = (int64_t)((M + 255) / 256) * ((N + 255) / 256);
+  return t256 >= 512 ? TILE_256 : TILE_128;
+}
 
 hipError_t launch_gemm(bool is_bf16, int a_kmajor, int b_kmajor, int tile, int splits, int tag,
                        const GemmParams& p, hipStream_t s) {

@@ -38,6 +38,8 @@ enum GemmTile { TILE_128 = 0, TILE_256 = 1, TILE_256x128 = 2 };
 hipError_t launch_gemm(bool is_bf16, int a_kmajor, int b_kmajor, int tile, int splits, int tag,
                        const GemmParams& p, hipStream_t s);
 int gemm_k_tile(bool is_bf16);
+// Measured tile choice for a bf16 product with an M x N output.
+int gemm_pick_tile(int M, int N);
 
 // Sum split-K partials: C[m, n] = alpha * sum_z part[z][m, n] + beta * C[m, n] (fixed z order).
 hipError_t launch_splitk_reduce(const float* part, int splits, int64_t split_stride, int M, int N,
@@ -69,6 +71,11 @@ hipError_t launch_colsum_partial(bool src_bf16, int M, int N, const void* src, i
 // out[j] = (accumulate ? out[j] : 0) + sum_p part[p * stride + j], fixed p order, j < n.
 hipError_t launch_colsum_reduce(const float* part, int nparts, int64_t stride, int n, float* out,
                                 int accumulate, hipStream_t s);
+// The same over columns [0, k*seg) of the partial rows, column j going to out_{j/seg}[j%seg]
+// (k = number of non-null outputs among out0, out1, out2, given in that order).
+hipError_t launch_colsum_reduce3(const float* part, int nparts, int64_t stride, int seg,
+                                 float* out0, float* out1, float* out2, int accumulate,
+                                 hipStream_t s);
 
 // ------------------------------------------------------------------------------ loss
 // logits (M, Vp) T, overwritten by softmax - onehot (pad columns 0); row_loss (M).

@@ -181,13 +181,42 @@ __global__ __launch_bounds__(256) void colsum_partial_kernel(int M, int N,
   }
 }
 
-__global__ void colsum_reduce_kernel(const float* __restrict__ part, int nparts, int64_t stride,
-                                     int n, float* __restrict__ out, int accumulate) {
-  const int j = blockIdx.x * blockDim.x + threadIdx.x;
-  if (j >= n) return;
-  float s = 0.0f;
-  for (int p = 0; p < nparts; ++p) s += part[(int64_t)p * stride + j];
-  out[j] = accumulate ? out[j] + s : s;
+// Sum of nparts partial rows per column. One block = 16 waves over 64 columns; wave w adds the
+// partials w, w+16, w+32, ... (four independent accumulators), then the 16 wave sums are added
+// in wave order. Columns [0, n) go to up to three outputs of `seg` columns each.
+struct ColOut {
+  float* out[3];
+};
+constexpr int RED_WAVES = 16;
+
+__global__ __launch_bounds__(64 * RED_WAVES) void colsum_reduce_kernel(
+    const float* __restrict__ part, int nparts, int64_t stride, int n, int seg, ColOut outs,
+    int accumulate) {
+  __shared__ float sh[RED_WAVES][64];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int j = blockIdx.x * 64 + lane;
+  float a0 = 0.0f, a1 = 0.0f, a2 = 0.0f, a3 = 0.0f;
+  if (j < n) {
+    int p = wave;
+    for (; p + 3 * RED_WAVES < nparts; p += 4 * RED_WAVES) {
+      a0 += part[(int64_t)p * stride + j];
+      a1 += part[(int64_t)(p + RED_WAVES) * stride + j];
+      a2 += part[(int64_t)(p + 2 * RED_WAVES) * stride + j];
+      a3 += part[(int64_t)(p + 3 * RED_WAVES) * stride + j];
+    }
+    for (; p < nparts; p += RED_WAVES) a0 += part[(int64_t)p * stride + j];
+  }
+  sh[wave][lane] = (a0 + a1) + (a2 + a3);
+  __syncthreads();
+  if (wave == 0 && j < n) {
+    float s = 0.0f;
+    for (int w = 0; w < RED_WAVES; ++w) s += sh[w][lane];
+    float* o = outs.out[j / seg];
+    if (o) {
+      const int c = j % seg;
+      o[c] = accumulate ? o[c] + s : s;
+    }
+  }
 }
 
 }  // namespace
@@ -240,8 +269,17 @@ hipError_t launch_colsum_partial(bool src_bf16, int M, int N, const void* src, i
 
 hipError_t launch_colsum_reduce(const float* part, int nparts, int64_t stride, int n, float* out,
                                 int accumulate, hipStream_t s) {
-  if (n == 0) return hipSuccess;
-  hipLaunchKernelGGL(colsum_reduce_kernel, dim3((n + 255) / 256), dim3(256), 0, s, part, nparts,
-                     stride, n, out, accumulate);
+  return launch_colsum_reduce3(part, nparts, stride, n, out, nullptr, nullptr, accumulate, s);
+}
+
+hipError_t launch_colsum_reduce3(const float* part, int nparts, int64_t stride, int seg,
+                                 float* out0, float* out1, float* out2, int accumulate,
+                                 hipStream_t s) {
+  if (seg == 0) return hipSuccess;
+  const int nseg = out2 ? 3 : (out1 ? 2 : 1);
+  const int n = nseg * seg;
+  ColOut outs{{out0, out1, out2}};
+  hipLaunchKernelGGL(colsum_reduce_kernel, dim3((n + 63) / 64), dim3(64 * RED_WAVES), 0, s, part,
+                     nparts, stride, n, seg, outs, accumulate);
   return hipGetLastError();
 }
