@@ -33,8 +33,8 @@ gpt2_status fail(gpt2_status s, const std::string& msg) {
       return fail(GPT2_E_HIP, std::string(#x) + " failed: " + hipGetErrorString(e_)); \
   } while (0)
 
-constexpr int LN_ROWS_PER_BLOCK = 64;
-constexpr int COLSUM_ROWS_PER_BLOCK = 64;
+constexpr int LN_ROWS_PER_BLOCK = 16;
+constexpr int COLSUM_ROWS_PER_BLOCK = 16;
 constexpr int MAX_ROWS = 16384;
 constexpr int TIMING_CAP = 4096;
 
