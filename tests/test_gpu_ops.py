@@ -20,7 +20,9 @@ def _stored(torch, logical, kmajor_rows_are_k, dtype):
 
 
 LAYOUTS = [(1, 0), (1, 1), (0, 0), (0, 1)]
-SHAPES = [(200, 136, 72), (256, 256, 128), (1000, 520, 776), (4096, 2304, 768), (64, 768, 3072)]
+# (6104, 2296, 192): more 128x128 tiles than the chip holds at once, ragged in m and n
+SHAPES = [(200, 136, 72), (256, 256, 128), (1000, 520, 776), (4096, 2304, 768), (64, 768, 3072),
+          (6104, 2296, 192)]
 
 
 @pytest.mark.parametrize("layout", LAYOUTS)

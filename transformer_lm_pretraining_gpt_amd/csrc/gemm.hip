@@ -18,6 +18,8 @@
 //    so every MFMA reads k-contiguous 16-byte fragments.
 //  * Blocks are renumbered so that consecutive tiles share an XCD (8 XCDs, own L2 each) and
 //    walk the output in groups of 8 row-tiles for L2 reuse of A and B.
+#include <algorithm>
+
 #include "common.h"
 #include "kernels.h"
 
@@ -289,6 +291,16 @@ DEV void wait_vmcnt() {
   __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
   asm volatile("" ::: "memory");
 }
+// Wait until at most `after` slabs of LW loads each are still in flight (after <= A).
+template <int LW, int A>
+DEV void wait_slabs(int after) {
+  if constexpr (A == 0) {
+    wait_vmcnt<0>();
+  } else {
+    if (after >= A) wait_vmcnt<A * LW>();
+    else wait_slabs<LW, A - 1>(after);
+  }
+}
 DEV int tr_swz(int krow) { return (krow & 3) << 2; }
 
 // K-major LDS rows of RB bytes (RB = 128 or 64): chunk swizzle measured conflict-free on gfx950
@@ -351,11 +363,21 @@ struct DmaTile {
   }
 };
 
+// Epilogue through LDS, eight rows of the wave tile at a time: register group q (r = 4q..4q+3) of
+// every 32x32 accumulator holds rows 8q + 4h + e (h = lane / 32); those rows go to the wave's
+// LDS buffer in MFMA layout and come back in row layout, so that each lane applies the epilogue
+// to 4 consecutive columns and writes them with one vector store. The pitch is 8 floats more
+// than the row so that the two lane halves hit disjoint banks.
+template <int NB>
+constexpr int epi_pitch() { return NB * 32 + 8; }
+template <int NB>
+constexpr int epi_wave_bytes() { return 8 * epi_pitch<NB>() * 4; }
+
 template <int EPI, int MB, int NB>
 DEV void epilogue_rows(const f32x16 (&acc)[MB][NB], const GemmParams& p, float* buf, int row0,
                        int col0, int lane) {
   constexpr int WN = NB * 32;
-  constexpr int PITCH = WN + 4;  // floats; padding spreads the two lane halves over banks
+  constexpr int PITCH = epi_pitch<NB>();
   constexpr int V4 = WN / 4;     // float4 per row
   constexpr int RPP = 64 / V4;   // rows per pass
   const int h = lane >> 5, l32 = lane & 31;
@@ -364,56 +386,64 @@ DEV void epilogue_rows(const f32x16 (&acc)[MB][NB], const GemmParams& p, float* 
 #pragma unroll
   for (int i = 0; i < MB; ++i) {
 #pragma unroll
-    for (int j = 0; j < NB; ++j)
+    for (int q = 0; q < 4; ++q) {
 #pragma unroll
-      for (int r = 0; r < 16; ++r) buf[mfma_row(r, h) * PITCH + j * 32 + l32] = acc[i][j][r];
-    __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0): this wave's LDS writes are done
-    asm volatile("" ::: "memory");
+      for (int j = 0; j < NB; ++j)
 #pragma unroll
-    for (int pass = 0; pass < 32 / RPP; ++pass) {
-      const int rl = pass * RPP + lane / V4;
-      const int c4 = lane % V4;
-      const int row = row0 + i * 32 + rl;
-      const int col = col0 + c4 * 4;
-      const f32x4 v = *reinterpret_cast<const f32x4*>(buf + rl * PITCH + c4 * 4);
-      if (row < p.M && col < p.N) {
-        const int64_t o = (int64_t)row * p.ldc + col;
-        f32x4 bias = p.bias ? *reinterpret_cast<const f32x4*>(p.bias + col) : f32x4{0, 0, 0, 0};
-        float out[4];
-        if constexpr (EPI == EPI_STORE) {
+        for (int e = 0; e < 4; ++e) buf[(4 * h + e) * PITCH + j * 32 + l32] = acc[i][j][4 * q + e];
+      __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0): this wave's LDS writes are done
+      asm volatile("" ::: "memory");
 #pragma unroll
-          for (int e = 0; e < 4; ++e) out[e] = p.alpha * v[e] + bias[e];
-          st8(static_cast<bf16*>(p.C) + o, u32x2{pack_bf16(out[0], out[1]), pack_bf16(out[2], out[3])});
-        } else if constexpr (EPI == EPI_BIAS_GELU) {
-          float gl[4];
+      for (int pass = 0; pass < 8 / RPP; ++pass) {
+        const int rl = pass * RPP + lane / V4;
+        const int c4 = lane % V4;
+        const int row = row0 + i * 32 + 8 * q + rl;
+        const int col = col0 + c4 * 4;
+        const f32x4 v = *reinterpret_cast<const f32x4*>(buf + rl * PITCH + c4 * 4);
+        if (row < p.M && col < p.N) {
+          const int64_t o = (int64_t)row * p.ldc + col;
+          f32x4 bias = p.bias ? *reinterpret_cast<const f32x4*>(p.bias + col) : f32x4{0, 0, 0, 0};
+          float out[4];
+          if constexpr (EPI == EPI_STORE) {
 #pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            out[e] = v[e] + bias[e];
-            gl[e] = gelu_tanh(out[e]);
+            for (int e = 0; e < 4; ++e) out[e] = p.alpha * v[e] + bias[e];
+            st8(static_cast<bf16*>(p.C) + o, u32x2{pack_bf16(out[0], out[1]), pack_bf16(out[2], out[3])});
+          } else if constexpr (EPI == EPI_BIAS_GELU) {
+            float gl[4];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              out[e] = v[e] + bias[e];
+              gl[e] = gelu_tanh(out[e]);
+            }
+            st8(static_cast<bf16*>(p.C) + o, u32x2{pack_bf16(out[0], out[1]), pack_bf16(out[2], out[3])});
+            st8(static_cast<bf16*>(p.C2) + o, u32x2{pack_bf16(gl[0], gl[1]), pack_bf16(gl[2], gl[3])});
+          } else if constexpr (EPI == EPI_BIAS_RESID) {
+            const f32x4 rs = *reinterpret_cast<const f32x4*>(p.resid + o);
+            *reinterpret_cast<f32x4*>(cf + o) = rs + v + bias;
+          } else if constexpr (EPI == EPI_GELU_BWD) {
+            const u32x2 u = ld8(static_cast<const bf16*>(p.aux) + o);
+            const float uf[4] = {bf16lo(u[0]), bf16hi(u[0]), bf16lo(u[1]), bf16hi(u[1])};
+#pragma unroll
+            for (int e = 0; e < 4; ++e) out[e] = v[e] * gelu_tanh_grad(uf[e]);
+            st8(static_cast<bf16*>(p.C) + o, u32x2{pack_bf16(out[0], out[1]), pack_bf16(out[2], out[3])});
+          } else {
+            f32x4 prev = f32x4{0, 0, 0, 0};
+            if (p.beta != 0.0f) prev = p.beta * *reinterpret_cast<const f32x4*>(cf + o);
+            *reinterpret_cast<f32x4*>(cf + o) = p.alpha * v + prev;
           }
-          st8(static_cast<bf16*>(p.C) + o, u32x2{pack_bf16(out[0], out[1]), pack_bf16(out[2], out[3])});
-          st8(static_cast<bf16*>(p.C2) + o, u32x2{pack_bf16(gl[0], gl[1]), pack_bf16(gl[2], gl[3])});
-        } else if constexpr (EPI == EPI_BIAS_RESID) {
-          const f32x4 rs = *reinterpret_cast<const f32x4*>(p.resid + o);
-          *reinterpret_cast<f32x4*>(cf + o) = rs + v + bias;
-        } else if constexpr (EPI == EPI_GELU_BWD) {
-          const u32x2 u = ld8(static_cast<const bf16*>(p.aux) + o);
-          const float uf[4] = {bf16lo(u[0]), bf16hi(u[0]), bf16lo(u[1]), bf16hi(u[1])};
-#pragma unroll
-          for (int e = 0; e < 4; ++e) out[e] = v[e] * gelu_tanh_grad(uf[e]);
-          st8(static_cast<bf16*>(p.C) + o, u32x2{pack_bf16(out[0], out[1]), pack_bf16(out[2], out[3])});
-        } else {
-          f32x4 prev = f32x4{0, 0, 0, 0};
-          if (p.beta != 0.0f) prev = p.beta * *reinterpret_cast<const f32x4*>(cf + o);
-          *reinterpret_cast<f32x4*>(cf + o) = p.alpha * v + prev;
         }
       }
+      __builtin_amdgcn_s_waitcnt(0xc07f);
+      asm volatile("" ::: "memory");
     }
-    __builtin_amdgcn_s_waitcnt(0xc07f);
-    asm volatile("" ::: "memory");
   }
 }
 
+// Persistent tiles: the grid holds at most as many blocks as fit on the chip at once, and each
+// block walks a strided sequence of output tiles (see the XCD partition below). Slabs go to stage
+// (slab count so far) mod NSTAGE across tiles, so when a tile's k loop ends the stage of its last
+// slab is free while the next tile's first NSTAGE-1 slabs go to the others: those loads are issued
+// first and stream in while the finished tile is written out through the free stage.
 template <int AK, int BKM, int BM, int BN, int RB, int NSTAGE, int MINB, int TAG>
 __global__ __launch_bounds__(THREADS, MINB) void gemm_dma_kernel(GemmParams p) {
   constexpr int WM = BM / 2, WN = BN / 2;
@@ -424,6 +454,7 @@ __global__ __launch_bounds__(THREADS, MINB) void gemm_dma_kernel(GemmParams p) {
   using TA = DmaTile<BM, AK == 1, RB>;
   using TB = DmaTile<BN, BKM == 1, RB>;
   constexpr int LW = TA::PER_WAVE + TB::PER_WAVE;  // loads per wave per slab
+  static_assert(4 * epi_wave_bytes<NB>() <= STAGE, "epilogue buffer must fit one stage");
   __shared__ __attribute__((aligned(1024))) char smem[NSTAGE * STAGE];
 
   const int tid = threadIdx.x, lane = tid & 63;
@@ -431,16 +462,26 @@ __global__ __launch_bounds__(THREADS, MINB) void gemm_dma_kernel(GemmParams p) {
 
   const int tiles_m = (p.M + BM - 1) / BM, tiles_n = (p.N + BN - 1) / BN;
   const int nblk = tiles_m * tiles_n;
-  int bid = blockIdx.x;
-  if ((nblk & 7) == 0) bid = (bid & 7) * (nblk >> 3) + (bid >> 3);
-  constexpr int GROUP = 8;
+  // Work items are output tiles in grouped order (GROUP row-tiles walked column by column). Block
+  // b runs on XCD b mod 8; when the grid is a multiple of 8, XCD x owns the contiguous run of
+  // items [x * per_xcd, (x + 1) * per_xcd) and its G/8 blocks stride through it, so each XCD's L2
+  // keeps its own row panels of A and streams the columns of B once.
+  const int G = gridDim.x;
+  const int b = blockIdx.x;
+  int w, w_end, stride;
+  if ((G & 7) == 0) {
+    const int per_xcd = (nblk + 7) >> 3;
+    w = (b & 7) * per_xcd + (b >> 3);
+    w_end = min(nblk, ((b & 7) + 1) * per_xcd);
+    stride = G >> 3;
+  } else {
+    w = b;
+    w_end = nblk;
+    stride = G;
+  }
+  if (w >= w_end) return;
+  const int GROUP = tiles_m <= 8 ? tiles_m : (tiles_m + 7) / 8;
   const int in_group = GROUP * tiles_n;
-  const int g = bid / in_group;
-  const int first_m = g * GROUP;
-  const int gsize = min(tiles_m - first_m, GROUP);
-  const int tm = first_m + (bid % in_group) % gsize;
-  const int tn = (bid % in_group) / gsize;
-  const int m0 = tm * BM, n0 = tn * BN;
   const int k_begin = blockIdx.z * p.k_split;
   const int k_end = min(p.K, k_begin + p.k_split);
   const int nk = (k_end - k_begin) / KT;
@@ -449,79 +490,98 @@ __global__ __launch_bounds__(THREADS, MINB) void gemm_dma_kernel(GemmParams p) {
   const bf16* B = static_cast<const bf16*>(p.B);
   const int wm0 = (wave >> 1) * WM, wn0 = (wave & 1) * WN;
 
-  f32x16 acc[MB][NB];
-#pragma unroll
-  for (int i = 0; i < MB; ++i)
-#pragma unroll
-    for (int j = 0; j < NB; ++j) acc[i][j] = f32x16{};
+  // output tile of work item w
+  auto tile_origin = [&](int item, int& m0, int& n0) {
+    const int g = item / in_group;
+    const int first_m = g * GROUP;
+    const int gsize = min(tiles_m - first_m, GROUP);
+    m0 = (first_m + (item % in_group) % gsize) * BM;
+    n0 = ((item % in_group) / gsize) * BN;
+  };
+  // slab `ks` of the tile at (m0, n0) into stage `st`
+  auto issue = [&](int m0, int n0, int ks, int st) {
+    char* dst = smem + st * STAGE;
+    TA::issue(A, p.lda, m0, p.M, k_begin + ks * KT, dst, wave, lane);
+    TB::issue(B, p.ldb, n0, p.N, k_begin + ks * KT, dst + BM * RB, wave, lane);
+  };
 
+  int m0, n0;
+  tile_origin(w, m0, n0);
+  int base = 0;  // stage of this tile's slab 0
 #pragma unroll
-  for (int s = 0; s < NSTAGE - 1; ++s) {
-    if (s < nk) {
-      char* st = smem + s * STAGE;
-      TA::issue(A, p.lda, m0, p.M, k_begin + s * KT, st, wave, lane);
-      TB::issue(B, p.ldb, n0, p.N, k_begin + s * KT, st + BM * RB, wave, lane);
-    }
-  }
-  for (int kt = 0; kt < nk; ++kt) {
-    // slabs issued after kt: min(NSTAGE - 2, nk - 1 - kt)
-    const int after = min(NSTAGE - 2, nk - 1 - kt);
-    if constexpr (NSTAGE >= 4) {
-      if (after >= 2) wait_vmcnt<2 * LW>();
-      else if (after == 1) wait_vmcnt<LW>();
-      else wait_vmcnt<0>();
-    } else if constexpr (NSTAGE == 3) {
-      if (after >= 1) wait_vmcnt<LW>();
-      else wait_vmcnt<0>();
-    } else {
-      wait_vmcnt<0>();
-    }
-    wave_barrier_all();
-    const int nxt = kt + NSTAGE - 1;
-    if (nxt < nk) {
-      char* st = smem + (nxt % NSTAGE) * STAGE;
-      TA::issue(A, p.lda, m0, p.M, k_begin + nxt * KT, st, wave, lane);
-      TB::issue(B, p.ldb, n0, p.N, k_begin + nxt * KT, st + BM * RB, wave, lane);
-    }
-    const char* sa = smem + (kt % NSTAGE) * STAGE;
-    const char* sb = sa + BM * RB;
-    // fragments of k-step s+1 are read while the MFMAs of k-step s run
-    u32x4 fa[2][MB], fb[2][NB];
+  for (int s = 0; s < NSTAGE - 1; ++s)
+    if (s < nk) issue(m0, n0, s, s);
+
+  while (true) {
+    f32x16 acc[MB][NB];
 #pragma unroll
-    for (int i = 0; i < MB; ++i) fa[0][i] = TA::frag(sa, wm0 + i * 32, 0, lane);
+    for (int i = 0; i < MB; ++i)
 #pragma unroll
-    for (int j = 0; j < NB; ++j) fb[0][j] = TB::frag(sb, wn0 + j * 32, 0, lane);
+      for (int j = 0; j < NB; ++j) acc[i][j] = f32x16{};
+
+    for (int kt = 0; kt < nk; ++kt) {
+      // slabs of this tile issued after slab kt: min(NSTAGE - 2, nk - 1 - kt); loads complete in
+      // issue order, so waiting until at most that many slabs' loads are pending (stores of the
+      // previous tile's epilogue only add to the count) means slab kt has landed
+      const int after = min(NSTAGE - 2, nk - 1 - kt);
+      wait_slabs<LW, NSTAGE - 2>(after);
+      wave_barrier_all();
+      const int nxt = kt + NSTAGE - 1;
+      if (nxt < nk) issue(m0, n0, nxt, (base + nxt) % NSTAGE);
+      const char* sa = smem + ((base + kt) % NSTAGE) * STAGE;
+      const char* sb = sa + BM * RB;
+      // fragments of k-step s+1 are read while the MFMAs of k-step s run
+      u32x4 fa[2][MB], fb[2][NB];
 #pragma unroll
-    for (int s = 0; s < KSTEPS; ++s) {
-      const int cur = s & 1;
-      if (s < KSTEPS - 1) {
+      for (int i = 0; i < MB; ++i) fa[0][i] = TA::frag(sa, wm0 + i * 32, 0, lane);
 #pragma unroll
-        for (int i = 0; i < MB; ++i) fa[cur ^ 1][i] = TA::frag(sa, wm0 + i * 32, s + 1, lane);
+      for (int j = 0; j < NB; ++j) fb[0][j] = TB::frag(sb, wn0 + j * 32, 0, lane);
 #pragma unroll
-        for (int j = 0; j < NB; ++j) fb[cur ^ 1][j] = TB::frag(sb, wn0 + j * 32, s + 1, lane);
+      for (int s = 0; s < KSTEPS; ++s) {
+        const int cur = s & 1;
+        if (s < KSTEPS - 1) {
+#pragma unroll
+          for (int i = 0; i < MB; ++i) fa[cur ^ 1][i] = TA::frag(sa, wm0 + i * 32, s + 1, lane);
+#pragma unroll
+          for (int j = 0; j < NB; ++j) fb[cur ^ 1][j] = TB::frag(sb, wn0 + j * 32, s + 1, lane);
+        }
+        // keep the reads of step s+1 ahead of the MFMAs of step s (the default scheduler would
+        // sink them to their use and expose the LDS latency every few MFMAs)
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int i = 0; i < MB; ++i)
+#pragma unroll
+          for (int j = 0; j < NB; ++j) Mfma<bf16>::mma(acc[i][j], fa[cur][i], fb[cur][j]);
+        __builtin_amdgcn_sched_barrier(0);
       }
-      // keep the reads of step s+1 ahead of the MFMAs of step s (the default scheduler would
-      // sink them to their use and expose the LDS latency every few MFMAs)
-      __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-      for (int i = 0; i < MB; ++i)
-#pragma unroll
-        for (int j = 0; j < NB; ++j) Mfma<bf16>::mma(acc[i][j], fa[cur][i], fb[cur][j]);
-      __builtin_amdgcn_sched_barrier(0);
     }
-  }
 
-  // all waves are done reading the stages: reuse the LDS for the epilogue
-  wait_vmcnt<0>();
-  wave_barrier_all();
-  float* buf = reinterpret_cast<float*>(smem) + wave * 32 * (WN + 4);
-  const int row0 = m0 + wm0, col0 = n0 + wn0;
-  switch (p.epi) {
-    case EPI_STORE: epilogue_rows<EPI_STORE, MB, NB>(acc, p, buf, row0, col0, lane); break;
-    case EPI_BIAS_GELU: epilogue_rows<EPI_BIAS_GELU, MB, NB>(acc, p, buf, row0, col0, lane); break;
-    case EPI_BIAS_RESID: epilogue_rows<EPI_BIAS_RESID, MB, NB>(acc, p, buf, row0, col0, lane); break;
-    case EPI_GELU_BWD: epilogue_rows<EPI_GELU_BWD, MB, NB>(acc, p, buf, row0, col0, lane); break;
-    default: epilogue_rows<EPI_F32, MB, NB>(acc, p, buf, row0, col0, lane); break;
+    // every wave is done reading this tile's stages; the last one becomes the epilogue buffer
+    wave_barrier_all();
+    const int last = (base + nk + NSTAGE - 1) % NSTAGE;
+    const int nbase = (base + nk) % NSTAGE;
+    const int wnext = w + stride;
+    int m1 = 0, n1 = 0;
+    if (wnext < w_end) {
+      tile_origin(wnext, m1, n1);
+#pragma unroll
+      for (int s = 0; s < NSTAGE - 1; ++s)
+        if (s < nk) issue(m1, n1, s, (nbase + s) % NSTAGE);
+    }
+    float* buf = reinterpret_cast<float*>(smem + last * STAGE + wave * epi_wave_bytes<NB>());
+    const int row0 = m0 + wm0, col0 = n0 + wn0;
+    switch (p.epi) {
+      case EPI_STORE: epilogue_rows<EPI_STORE, MB, NB>(acc, p, buf, row0, col0, lane); break;
+      case EPI_BIAS_GELU: epilogue_rows<EPI_BIAS_GELU, MB, NB>(acc, p, buf, row0, col0, lane); break;
+      case EPI_BIAS_RESID: epilogue_rows<EPI_BIAS_RESID, MB, NB>(acc, p, buf, row0, col0, lane); break;
+      case EPI_GELU_BWD: epilogue_rows<EPI_GELU_BWD, MB, NB>(acc, p, buf, row0, col0, lane); break;
+      default: epilogue_rows<EPI_F32, MB, NB>(acc, p, buf, row0, col0, lane); break;
+    }
+    if (wnext >= w_end) break;
+    w = wnext;
+    m0 = m1;
+    n0 = n1;
+    base = nbase;
   }
 }
 
@@ -541,23 +601,42 @@ __global__ void splitk_reduce_kernel(const float* __restrict__ part, int splits,
 // Tile configurations of the direct-to-LDS kernel: 256x256 with 128-byte slabs, two stages
 // (128 KB LDS, one block per CU); 256x128 and 128x128 with 64-byte slabs, three stages (72 / 48 KB
 // LDS), two blocks per CU so that one block's epilogue overlaps the other's MFMAs.
+// Blocks of `kernel` resident at once on the current device (CUs x blocks per CU).
+template <typename K>
+int resident_blocks(K kernel) {
+  int dev = 0, cus = 0, per_cu = 0;
+  if (hipGetDevice(&dev) != hipSuccess ||
+      hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+      hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kernel, THREADS, 0) != hipSuccess)
+    return 256;
+  return std::max(1, cus * std::max(per_cu, 1));
+}
+
+template <void (*KERNEL)(GemmParams)>
+hipError_t launch_persistent(int tiles, int splits, const GemmParams& p, hipStream_t s) {
+  static const int resident = resident_blocks(KERNEL);  // one value per kernel
+  const int per_z = std::max(1, resident / splits);
+  dim3 grid(std::min(tiles, per_z), 1, splits), block(THREADS);
+  hipLaunchKernelGGL(KERNEL, grid, block, 0, s, p);
+  return hipGetLastError();
+}
+
+// Tile configurations of the direct-to-LDS kernel: 256x256 with 128-byte slabs, two stages
+// (128 KB LDS, one block per CU); 256x128 and 128x128 with 64-byte slabs, three stages (72 / 48 KB
+// LDS), two or three blocks per CU so that one block's epilogue overlaps another's MFMAs.
 template <int AK, int BKM, int BM, int BN>
 hipError_t launch_dma(int splits, int tag, const GemmParams& p, hipStream_t s) {
   constexpr int RB = (BM == 256 && BN == 256) ? 128 : 64;
   constexpr int STAGE = (BM + BN) * RB;
   constexpr int NSTAGE = (BM == 256 && BN == 256) ? 2 : 3;
   constexpr int MINB = (BM == 256 && BN == 256) ? 1 : 2;
-  static_assert(NSTAGE * STAGE <= 160 * 1024, "LDS");
+  static_assert(NSTAGE * STAGE * MINB <= 160 * 1024, "LDS");
   const int tiles = ((p.M + BM - 1) / BM) * ((p.N + BN - 1) / BN);
-  dim3 grid(tiles, 1, splits), block(THREADS);
   if constexpr (AK == 1 && BKM == 1 && BM == 256 && BN == 256) {
-    if (tag == 1) {
-      hipLaunchKernelGGL((gemm_dma_kernel<AK, BKM, BM, BN, RB, NSTAGE, MINB, 1>), grid, block, 0, s, p);
-      return hipGetLastError();
-    }
+    if (tag == 1)
+      return launch_persistent<gemm_dma_kernel<AK, BKM, BM, BN, RB, NSTAGE, MINB, 1>>(tiles, splits, p, s);
   }
-  hipLaunchKernelGGL((gemm_dma_kernel<AK, BKM, BM, BN, RB, NSTAGE, MINB, 0>), grid, block, 0, s, p);
-  return hipGetLastError();
+  return launch_persistent<gemm_dma_kernel<AK, BKM, BM, BN, RB, NSTAGE, MINB, 0>>(tiles, splits, p, s);
 }
 
 template <typename T, int AK, int BKM, int BM, int BN>
