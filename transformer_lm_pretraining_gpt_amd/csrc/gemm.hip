@@ -5,19 +5,17 @@
 // forward and both backward products are matmuls of the forward's size). The tied LM head is the
 // same kernel with the (Vp, d) embedding as the B operand.
 //
-// Design:
-//  * 256 threads = 4 waves in a 2 x 2 arrangement; block tile BM x BN, wave tile BM/2 x BN/2 made
-//    of 32 x 32 MFMA tiles (v_mfma_f32_32x32x16_bf16, or 4 x v_mfma_f32_32x32x2f32 for fp32).
-//  * K advances in 128-byte slabs (64 bf16 or 32 fp32). Each operand tile lives in LDS as rows of
-//    128 bytes, k contiguous, with the 16-byte chunk index XOR-swizzled by (row/2) mod 8 so
-//    that both the fills and the MFMA fragment reads are free of bank conflicts.
-//  * Two LDS stages: the global loads of slab k+1 are issued before the MFMAs of slab k and land
-//    in registers; they are written to the other stage after the MFMAs; one barrier per slab.
-//  * Operands whose k is the strided dimension (the weight in x W, and both operands of X^T dY)
-//    are loaded along their contiguous dimension and transposed in registers on the way to LDS,
-//    so every MFMA reads k-contiguous 16-byte fragments.
-//  * Blocks are renumbered so that consecutive tiles share an XCD (8 XCDs, own L2 each) and
-//    walk the output in groups of 8 row-tiles for L2 reuse of A and B.
+// Two kernels share the block shape: 256 threads = 4 waves in a 2 x 2 arrangement, block tile
+// BM x BN, wave tile BM/2 x BN/2 made of 32 x 32 MFMA tiles (v_mfma_f32_32x32x16_bf16, or
+// 4 x v_mfma_f32_32x32x2f32 for fp32), and the same fused epilogues.
+//  * gemm_kernel (fp32, and bf16 when K is not a multiple of 64): 128-byte slabs loaded through
+//    registers, transposed in registers where k is the strided dimension, written to one of two
+//    XOR-swizzled LDS stages; one barrier per slab.
+//  * gemm_dma_kernel (bf16, K a multiple of 64): persistent blocks, loads straight from memory
+//    into three LDS stages, spread through the MFMAs, and an epilogue that overlaps the next
+//    tile's first loads; details at its definition below.
+// Both walk output tiles in groups of row-tiles column by column for L2 reuse, with each of the
+// 8 XCDs (own L2 each) working on its own contiguous part of that order.
 #include <algorithm>
 
 #include "common.h"
@@ -262,10 +260,14 @@ __global__ __launch_bounds__(THREADS) void gemm_kernel(GemmParams p) {
 }
 
 // ------------------------------------------------------------------------------------------
-// bf16 product with direct global->LDS loads (global_load_lds_dwordx4), for K a multiple of 64.
+// bf16 product with direct global->LDS loads (buffer_load_dwordx4 ... lds), for K a multiple of 64.
 //
 // Each 16-byte load goes straight into LDS (no staging registers, no LDS write instructions),
-// so NSTAGE slabs can be in flight. K-major tiles use the XOR-swizzled 128-byte rows above.
+// so NSTAGE slabs can be in flight. Loads address memory through a buffer resource set to the
+// slab's origin (scalar registers) plus a 32-bit per-lane offset computed once per tile, so a load
+// costs no vector address arithmetic; a load still occupies its SIMD for a few tens of cycles
+// (measured: ~5% of 16 MFMAs per 1 KB load), so each slab's loads are spread evenly through the
+// MFMAs of the previous slab instead of being issued in one burst. K-major tiles use the XOR-swizzled 128-byte rows above.
 // Tiles stored k-row by k-row ([k][r], r contiguous) are copied as they are, with 16-byte chunk c
 // of k-row k placed at chunk c ^ 4(k mod 4); their MFMA fragments are read with
 // ds_read_b64_tr_b16, which hands each lane four consecutive k of one row: within a group of 16
@@ -276,8 +278,13 @@ __global__ __launch_bounds__(THREADS) void gemm_kernel(GemmParams p) {
 typedef __attribute__((address_space(3))) void lds_void_t;
 typedef __attribute__((ext_vector_type(4))) short s16x4;
 
-DEV void lds_dma16(const void* g, char* lds_wave_base) {
-  __builtin_amdgcn_global_load_lds(g, (lds_void_t*)lds_wave_base, 16, 0, 0);
+// Raw buffer resource at byte address `p`: offsets up to 2^31 - 1, no format conversion.
+DEV __amdgpu_buffer_rsrc_t buffer_at(const void* p) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), (short)0, 0x7fffffff, 0x00020000);
+}
+// 16 bytes per lane from the buffer at byte offset `voff` into LDS at `lds_wave_base` + 16 * lane.
+DEV void lds_dma16(__amdgpu_buffer_rsrc_t r, uint32_t voff, char* lds_wave_base) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void_t*)lds_wave_base, 16, voff, 0, 0, 0);
 }
 DEV void wave_barrier_all() {
   asm volatile("" ::: "memory");
@@ -316,30 +323,40 @@ template <int R, bool KMAJOR, int RB>
 struct DmaTile {
   static constexpr int KT = RB / 2;                  // k per slab
   static constexpr int PER_WAVE = R * RB / 4096;     // 1 KB wave-loads per slab per wave
-  // Issue this wave's loads of one slab (k0 .. k0+KT-1) into the stage buffer `dst`.
-  DEV static void issue(const bf16* __restrict__ base, int64_t ld, int r0, int r_total, int k0,
-                        char* dst, int wave, int lane) {
+  static constexpr int DS_PER_FRAG = KMAJOR ? 1 : 2;  // LDS read instructions per fragment
+  // Byte offsets, relative to the slab origin of the tile starting at row r0, of this wave's
+  // loads (one per 1 KB wave-load). They depend on the tile (rows past the matrix are clamped to
+  // its last row or 8-column group, in bounds; their results are never stored), not on the slab.
+  DEV static void offsets(uint32_t (&off)[PER_WAVE], int64_t ld, int r0, int r_total, int wave,
+                          int lane) {
 #pragma unroll
     for (int i = 0; i < PER_WAVE; ++i) {
       const int q = wave * PER_WAVE + i;
-      const bf16* g;
       if constexpr (KMAJOR) {
         constexpr int CPR = RB / 16, RPI = 1024 / RB;  // chunks per row, rows per wave-load
         const int row = RPI * q + lane / CPR;
         const int c = (lane % CPR) ^ swz_rb<RB>(row);
         const int r = min(r0 + row, r_total - 1);
-        g = base + (int64_t)r * ld + k0 + c * 8;
+        off[i] = (uint32_t)((int64_t)(r - r0) * ld * 2 + c * 16);
       } else {
         constexpr int CPR = R / 8;            // 16-byte chunks per k-row
         constexpr int KPI = 1024 / (2 * R);   // k-rows per wave-load
         const int krow = q * KPI + lane / CPR;
         const int c = (lane % CPR) ^ tr_swz(krow);
         int r = r0 + c * 8;
-        if (r >= r_total) r = r_total - 8;
-        g = base + (int64_t)(k0 + krow) * ld + r;
+        if (r >= r_total) r = r_total - 8;  // r_total and r0 are multiples of 8: r >= r0
+        off[i] = (uint32_t)((int64_t)krow * ld * 2 + (r - r0) * 2);
       }
-      lds_dma16(g, dst + q * 1024);
     }
+  }
+  // Buffer resource at the origin of the slab (rows from r0, k from k0).
+  DEV static __amdgpu_buffer_rsrc_t slab(const bf16* base, int64_t ld, int r0, int k0) {
+    return buffer_at(KMAJOR ? base + (int64_t)r0 * ld + k0 : base + (int64_t)k0 * ld + r0);
+  }
+  // Load i of this wave's part of a slab into the stage `dst`.
+  DEV static void issue(__amdgpu_buffer_rsrc_t r, const uint32_t (&off)[PER_WAVE], int i, char* dst,
+                        int wave) {
+    lds_dma16(r, off[i], dst + (wave * PER_WAVE + i) * 1024);
   }
   // Fragment (32 rows from rw, k = 16s .. 16s+15 of the slab) for the calling lane.
   DEV static u32x4 frag(const char* st, int rw, int s, int lane) {
@@ -439,6 +456,64 @@ DEV void epilogue_rows(const f32x16 (&acc)[MB][NB], const GemmParams& p, float* 
   }
 }
 
+// Scheduling pattern for one k-step: NM MFMAs with ND LDS reads and NV buffer loads spread evenly
+// between them.
+template <int NM, int ND, int NV, int Q = 0>
+DEV void interleave() {
+  if constexpr (Q < NM) {
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one MFMA
+    constexpr int d = (Q + 1) * ND / NM - Q * ND / NM;
+    if constexpr (d > 0) __builtin_amdgcn_sched_group_barrier(0x100, d, 0);  // LDS reads
+    constexpr int v = (Q + 1) * NV / NM - Q * NV / NM;
+    if constexpr (v > 0) __builtin_amdgcn_sched_group_barrier(0x010, v, 0);  // buffer loads
+    interleave<NM, ND, NV, Q + 1>();
+  }
+}
+
+// MFMAs of one slab (KSTEPS k-steps of 16) on the stage (sa, sb). Fragments of k-step s+1 are
+// read during k-step s; with ISSUE, the loads of a later slab into (dst_a, dst_b) are spread over
+// the k-steps, PER_WAVE / KSTEPS per operand each.
+template <bool ISSUE, class TA, class TB, int MB, int NB, int KSTEPS>
+DEV void slab_mma(f32x16 (&acc)[MB][NB], const char* sa, const char* sb, int wm0, int wn0,
+                  int lane, int wave, __amdgpu_buffer_rsrc_t ra, __amdgpu_buffer_rsrc_t rb,
+                  const uint32_t (&offa)[TA::PER_WAVE], const uint32_t (&offb)[TB::PER_WAVE],
+                  char* dst_a, char* dst_b) {
+  constexpr int LA = TA::PER_WAVE / KSTEPS, LB = TB::PER_WAVE / KSTEPS;
+  static_assert(LA * KSTEPS == TA::PER_WAVE && LB * KSTEPS == TB::PER_WAVE, "even load split");
+  constexpr int NM = MB * NB;
+  constexpr int ND = MB * TA::DS_PER_FRAG + NB * TB::DS_PER_FRAG;
+  constexpr int NV = ISSUE ? LA + LB : 0;
+  u32x4 fa[2][MB], fb[2][NB];
+#pragma unroll
+  for (int i = 0; i < MB; ++i) fa[0][i] = TA::frag(sa, wm0 + i * 32, 0, lane);
+#pragma unroll
+  for (int j = 0; j < NB; ++j) fb[0][j] = TB::frag(sb, wn0 + j * 32, 0, lane);
+  __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+  for (int s = 0; s < KSTEPS; ++s) {
+    const int cur = s & 1;
+    if (s < KSTEPS - 1) {
+#pragma unroll
+      for (int i = 0; i < MB; ++i) fa[cur ^ 1][i] = TA::frag(sa, wm0 + i * 32, s + 1, lane);
+#pragma unroll
+      for (int j = 0; j < NB; ++j) fb[cur ^ 1][j] = TB::frag(sb, wn0 + j * 32, s + 1, lane);
+    }
+    if constexpr (ISSUE) {
+#pragma unroll
+      for (int t = 0; t < LA; ++t) TA::issue(ra, offa, s * LA + t, dst_a, wave);
+#pragma unroll
+      for (int t = 0; t < LB; ++t) TB::issue(rb, offb, s * LB + t, dst_b, wave);
+    }
+#pragma unroll
+    for (int i = 0; i < MB; ++i)
+#pragma unroll
+      for (int j = 0; j < NB; ++j) Mfma<bf16>::mma(acc[i][j], fa[cur][i], fb[cur][j]);
+    if (s < KSTEPS - 1) interleave<NM, ND, NV>();
+    else interleave<NM, 0, NV>();
+    __builtin_amdgcn_sched_barrier(0);
+  }
+}
+
 // Persistent tiles: the grid holds at most as many blocks as fit on the chip at once, and each
 // block walks a strided sequence of output tiles (see the XCD partition below). Slabs go to stage
 // (slab count so far) mod NSTAGE across tiles, so when a tile's k loop ends the stage of its last
@@ -498,15 +573,22 @@ __global__ __launch_bounds__(THREADS, MINB) void gemm_dma_kernel(GemmParams p) {
     m0 = (first_m + (item % in_group) % gsize) * BM;
     n0 = ((item % in_group) / gsize) * BN;
   };
-  // slab `ks` of the tile at (m0, n0) into stage `st`
+  uint32_t offa[TA::PER_WAVE], offb[TB::PER_WAVE];  // this wave's load offsets for the tile
+  // whole slab `ks` of the tile at (m0, n0) into stage `st`
   auto issue = [&](int m0, int n0, int ks, int st) {
     char* dst = smem + st * STAGE;
-    TA::issue(A, p.lda, m0, p.M, k_begin + ks * KT, dst, wave, lane);
-    TB::issue(B, p.ldb, n0, p.N, k_begin + ks * KT, dst + BM * RB, wave, lane);
+    const __amdgpu_buffer_rsrc_t ra = TA::slab(A, p.lda, m0, k_begin + ks * KT);
+    const __amdgpu_buffer_rsrc_t rb = TB::slab(B, p.ldb, n0, k_begin + ks * KT);
+#pragma unroll
+    for (int i = 0; i < TA::PER_WAVE; ++i) TA::issue(ra, offa, i, dst, wave);
+#pragma unroll
+    for (int i = 0; i < TB::PER_WAVE; ++i) TB::issue(rb, offb, i, dst + BM * RB, wave);
   };
 
   int m0, n0;
   tile_origin(w, m0, n0);
+  TA::offsets(offa, p.lda, m0, p.M, wave, lane);
+  TB::offsets(offb, p.ldb, n0, p.N, wave, lane);
   int base = 0;  // stage of this tile's slab 0
 #pragma unroll
   for (int s = 0; s < NSTAGE - 1; ++s)
@@ -519,41 +601,29 @@ __global__ __launch_bounds__(THREADS, MINB) void gemm_dma_kernel(GemmParams p) {
 #pragma unroll
       for (int j = 0; j < NB; ++j) acc[i][j] = f32x16{};
 
-    for (int kt = 0; kt < nk; ++kt) {
-      // slabs of this tile issued after slab kt: min(NSTAGE - 2, nk - 1 - kt); loads complete in
-      // issue order, so waiting until at most that many slabs' loads are pending (stores of the
-      // previous tile's epilogue only add to the count) means slab kt has landed
-      const int after = min(NSTAGE - 2, nk - 1 - kt);
-      wait_slabs<LW, NSTAGE - 2>(after);
+    // slabs of this tile issued after slab kt: min(NSTAGE - 2, nk - 1 - kt); loads complete in
+    // issue order, so waiting until at most that many slabs' loads are pending (stores of the
+    // previous tile's epilogue only add to the count) means slab kt has landed. Slabs that still
+    // have a later slab to load (kt < nk - NSTAGE + 1) spread its loads over their MFMAs; the last
+    // NSTAGE - 1 slabs run in a loop of their own with no loads, so each loop has one body.
+    const int nmain = max(nk - (NSTAGE - 1), 0);
+    for (int kt = 0; kt < nmain; ++kt) {
+      wait_slabs<LW, NSTAGE - 2>(NSTAGE - 2);
       wave_barrier_all();
-      const int nxt = kt + NSTAGE - 1;
-      if (nxt < nk) issue(m0, n0, nxt, (base + nxt) % NSTAGE);
       const char* sa = smem + ((base + kt) % NSTAGE) * STAGE;
-      const char* sb = sa + BM * RB;
-      // fragments of k-step s+1 are read while the MFMAs of k-step s run
-      u32x4 fa[2][MB], fb[2][NB];
-#pragma unroll
-      for (int i = 0; i < MB; ++i) fa[0][i] = TA::frag(sa, wm0 + i * 32, 0, lane);
-#pragma unroll
-      for (int j = 0; j < NB; ++j) fb[0][j] = TB::frag(sb, wn0 + j * 32, 0, lane);
-#pragma unroll
-      for (int s = 0; s < KSTEPS; ++s) {
-        const int cur = s & 1;
-        if (s < KSTEPS - 1) {
-#pragma unroll
-          for (int i = 0; i < MB; ++i) fa[cur ^ 1][i] = TA::frag(sa, wm0 + i * 32, s + 1, lane);
-#pragma unroll
-          for (int j = 0; j < NB; ++j) fb[cur ^ 1][j] = TB::frag(sb, wn0 + j * 32, s + 1, lane);
-        }
-        // keep the reads of step s+1 ahead of the MFMAs of step s (the default scheduler would
-        // sink them to their use and expose the LDS latency every few MFMAs)
-        __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-        for (int i = 0; i < MB; ++i)
-#pragma unroll
-          for (int j = 0; j < NB; ++j) Mfma<bf16>::mma(acc[i][j], fa[cur][i], fb[cur][j]);
-        __builtin_amdgcn_sched_barrier(0);
-      }
+      const int nxt = kt + NSTAGE - 1;
+      char* dst = smem + ((base + nxt) % NSTAGE) * STAGE;
+      slab_mma<true, TA, TB, MB, NB, KSTEPS>(
+          acc, sa, sa + BM * RB, wm0, wn0, lane, wave, TA::slab(A, p.lda, m0, k_begin + nxt * KT),
+          TB::slab(B, p.ldb, n0, k_begin + nxt * KT), offa, offb, dst, dst + BM * RB);
+    }
+    for (int kt = nmain; kt < nk; ++kt) {
+      wait_slabs<LW, NSTAGE - 2>(nk - 1 - kt);
+      wave_barrier_all();
+      const char* sa = smem + ((base + kt) % NSTAGE) * STAGE;
+      const __amdgpu_buffer_rsrc_t unused = buffer_at(A);  // no loads left for this tile
+      slab_mma<false, TA, TB, MB, NB, KSTEPS>(acc, sa, sa + BM * RB, wm0, wn0, lane, wave, unused,
+                                              unused, offa, offb, nullptr, nullptr);
     }
 
     // every wave is done reading this tile's stages; the last one becomes the epilogue buffer
@@ -564,6 +634,8 @@ __global__ __launch_bounds__(THREADS, MINB) void gemm_dma_kernel(GemmParams p) {
     int m1 = 0, n1 = 0;
     if (wnext < w_end) {
       tile_origin(wnext, m1, n1);
+      TA::offsets(offa, p.lda, m1, p.M, wave, lane);
+      TB::offsets(offb, p.ldb, n1, p.N, wave, lane);
 #pragma unroll
       for (int s = 0; s < NSTAGE - 1; ++s)
         if (s < nk) issue(m1, n1, s, (nbase + s) % NSTAGE);
@@ -621,18 +693,20 @@ hipError_t launch_persistent(int tiles, int splits, const GemmParams& p, hipStre
   return hipGetLastError();
 }
 
-// Tile configurations of the direct-to-LDS kernel: 256x256 with 128-byte slabs, two stages
-// (128 KB LDS, one block per CU); 256x128 and 128x128 with 64-byte slabs, three stages (72 / 48 KB
-// LDS), two or three blocks per CU so that one block's epilogue overlaps another's MFMAs.
+// Tile configurations of the direct-to-LDS kernel, both with 64-byte slabs (32 k) and three
+// stages: 256x128 (72 KB LDS, two blocks per CU) and 128x128 (48 KB, up to three per CU). With
+// several blocks per CU one block's barriers and epilogue overlap another's MFMAs. Chosen by
+// measurement over the GPT-2 shapes against 256x256 tiles and deeper or shallower pipelines
+// (256x128 for the large products, 128x128 for the rest).
 template <int AK, int BKM, int BM, int BN>
 hipError_t launch_dma(int splits, int tag, const GemmParams& p, hipStream_t s) {
-  constexpr int RB = (BM == 256 && BN == 256) ? 128 : 64;
+  constexpr int RB = 64;
   constexpr int STAGE = (BM + BN) * RB;
-  constexpr int NSTAGE = (BM == 256 && BN == 256) ? 2 : 3;
-  constexpr int MINB = (BM == 256 && BN == 256) ? 1 : 2;
+  constexpr int NSTAGE = 3;
+  constexpr int MINB = 2;
   static_assert(NSTAGE * STAGE * MINB <= 160 * 1024, "LDS");
   const int tiles = ((p.M + BM - 1) / BM) * ((p.N + BN - 1) / BN);
-  if constexpr (AK == 1 && BKM == 1 && BM == 256 && BN == 256) {
+  if constexpr (AK == 1 && BKM == 1 && BM == 256 && BN == 128) {
     if (tag == 1)
       return launch_persistent<gemm_dma_kernel<AK, BKM, BM, BN, RB, NSTAGE, MINB, 1>>(tiles, splits, p, s);
   }
@@ -642,15 +716,16 @@ hipError_t launch_dma(int splits, int tag, const GemmParams& p, hipStream_t s) {
 template <typename T, int AK, int BKM, int BM, int BN>
 hipError_t launch_t(int splits, int tag, const GemmParams& p, hipStream_t s) {
   if constexpr (sizeof(T) == 2) {
-    // direct-to-LDS pipeline when every slab is a whole 64-wide k-slab and rows fit the tiles
+    // direct-to-LDS pipeline when every slab is a whole 64-wide k-slab, rows fit the tiles and
+    // 256 rows of either operand span less than 2 GiB (32-bit buffer offsets within a slab)
     if (p.K % 64 == 0 && (splits == 1 || p.k_split % 64 == 0) && p.M >= (AK ? 1 : 8) &&
-        p.N >= (BKM ? 1 : 8))
+        p.N >= (BKM ? 1 : 8) && p.lda < (1 << 22) && p.ldb < (1 << 22))
       return launch_dma<AK, BKM, BM, BN>(splits, tag, p, s);
   }
   const int tiles = ((p.M + BM - 1) / BM) * ((p.N + BN - 1) / BN);
   dim3 grid(tiles, 1, splits), block(THREADS);
   // tag 1: a separately named copy of the LM-head product, so profilers report it on its own
-  if constexpr (sizeof(T) == 2 && AK == 1 && BKM == 1 && BM == 256 && BN == 256) {
+  if constexpr (sizeof(T) == 2 && AK == 1 && BKM == 1 && BM == 256 && BN == 128) {
     if (tag == 1) {
       hipLaunchKernelGGL((gemm_kernel<T, AK, BKM, BM, BN, 1>), grid, block, 0, s, p);
       return hipGetLastError();
@@ -677,7 +752,6 @@ hipError_t launch_type(int a_kmajor, int b_kmajor, int tile, int splits, int tag
     return launch_layout<T, 128, 128>(a_kmajor, b_kmajor, splits, tag, p, s);
   } else {
     switch (tile) {
-      case TILE_256: return launch_layout<T, 256, 256>(a_kmajor, b_kmajor, splits, tag, p, s);
       case TILE_256x128: return launch_layout<T, 256, 128>(a_kmajor, b_kmajor, splits, tag, p, s);
       default: return launch_layout<T, 128, 128>(a_kmajor, b_kmajor, splits, tag, p, s);
     }
@@ -690,7 +764,7 @@ int gemm_k_tile(bool is_bf16) { return is_bf16 ? ROWB / 2 : ROWB / 4; }
 
 int gemm_pick_tile(int M, int N) {
   const int64_t t256 = (int64_t)((M + 255) / 256) * ((N + 255) / 256);
-  return t256 >= 512 ? TILE_256 : TILE_128;
+  return t256 >= 512 ? TILE_256x128 : TILE_128;
 }
 
 hipError_t launch_gemm(bool is_bf16, int a_kmajor, int b_kmajor, int tile, int splits, int tag,
