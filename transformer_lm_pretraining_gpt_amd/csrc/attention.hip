@@ -19,6 +19,7 @@
 
 #include "common.h"
 #include "kernels.h"
+#include "lds_dma.h"
 
 namespace {
 
@@ -256,6 +257,166 @@ __global__ __launch_bounds__(THREADS) void attn_fwd_kernel(const T* __restrict__
   if (h == 0 && qi < T_) lse[(int64_t)bh * T_ + qi] = (m_run + log2f(l_tot)) * LN2;
 }
 
+// ------------------------------------------------------- forward, bf16 with head_dim 64
+// Path for bf16 heads of 64 when T is a multiple of 64. K and V tiles of 64 keys go straight
+// from memory into a three-stage LDS ring; the K tile is read as K-major A fragments of S^T =
+// K Q^T, and the V tile, stored as it is ([key][d] rows), is read transposed with
+// ds_read_b64_tr_b16 as the A operand of O^T = V^T P^T, in the key order that the probability
+// registers already have. A block owns 256 queries; wave w owns the 32-query groups w and 7 - w,
+// so the four waves see about the same number of keys under the causal mask. Only the diagonal
+// tile of a group is masked, and the running output is rescaled only when some lane's maximum
+// grew (alpha = 1 otherwise, so skipping it changes nothing).
+constexpr int F64_Q = 256;        // queries per block
+constexpr int F64_NST = 3;        // LDS stages
+constexpr int F64_STAGE = 16384;  // K tile (8 KB) then V tile (8 KB)
+
+// A operand V^T[d0 + l%32][keys key0 + 4h + 0..3, key0 + 8 + 4h + 0..3] (h = l / 32) from a V
+// tile of [key][d] rows: the keys of probability registers p[8u .. 8u+7] of an S^T accumulator
+// (rows mfma_row(r, h)) for key0 = 32 js + 16 u.
+DEV u32x4 vt_frag(const char* vtile, int d0, int key0, int lane) {
+  const int g = lane >> 4, j = lane & 15;
+  const int r = d0 + (g & 1) * 16 + 4 * (j & 3);
+  const int chunk = r >> 3, within = (r & 7) * 2;
+  u32x2 out[2];
+#pragma unroll
+  for (int t = 0; t < 2; ++t) {
+    const int krow = key0 + 4 * (g >> 1) + 8 * t + (j >> 2);
+    const char* a = vtile + krow * 128 + ((chunk ^ tr_swz<64>(krow)) << 4) + within;
+    const s16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4*)(a));
+    out[t] = __builtin_bit_cast(u32x2, v);
+  }
+  return u32x4{out[0][0], out[0][1], out[1][0], out[1][1]};
+}
+
+__global__ __launch_bounds__(THREADS, 2) void attn_fwd64_kernel(const bf16* __restrict__ qkv,
+                                                                bf16* __restrict__ out,
+                                                                float* __restrict__ lse, int T_,
+                                                                int H) {
+  using TK = DmaTile<64, true, 128>;   // keys x d, K-major
+  using TV = DmaTile<64, false, 128>;  // [key][d] rows, read transposed
+  constexpr int LW = TK::PER_WAVE + TV::PER_WAVE;
+  __shared__ __attribute__((aligned(1024))) char smem[F64_NST * F64_STAGE];
+  const int tid = threadIdx.x, lane = tid & 63, h = lane >> 5, l32 = lane & 31;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int nqb = (T_ + F64_Q - 1) / F64_Q;
+  const int qb = nqb - 1 - (int)blockIdx.x;  // heaviest query blocks first
+  const int bh = blockIdx.y, b = bh / H, hh = bh % H;
+  const int dm = H * 64;
+  const int64_t ld = 3 * (int64_t)dm;
+  const bf16* Q = qkv + (int64_t)b * T_ * ld + hh * 64;
+  const bf16* K = Q + dm;
+  const bf16* V = Q + 2 * dm;
+  const int q0 = qb * F64_Q;
+  const int ntiles = min(T_, q0 + F64_Q) / 64;
+
+  int qg[2];
+  qg[0] = q0 + 32 * wave;
+  qg[1] = q0 + 32 * (7 - wave);
+  u32x4 qf[2][4];
+#pragma unroll
+  for (int i = 0; i < 2; ++i) load_row_frags<bf16, 64>(qf[i], Q, ld, qg[i] + l32, T_, h);
+  f32x16 o[2][2];
+  float m_run[2], l_run[2];
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    o[i][0] = o[i][1] = f32x16{};
+    m_run[i] = -INFINITY;
+    l_run[i] = 0.0f;
+  }
+  const float c = LOG2E / 8.0f;  // log2(e) / sqrt(64)
+
+  uint32_t offk[TK::PER_WAVE], offv[TV::PER_WAVE];
+  TK::offsets(offk, ld, 0, 64, wave, lane);
+  TV::offsets(offv, ld, 0, 64, wave, lane);
+  auto issue = [&](int kt) {
+    char* st = smem + (kt % F64_NST) * F64_STAGE;
+    const __amdgpu_buffer_rsrc_t rk = TK::slab(K, ld, kt * 64, 0);
+    const __amdgpu_buffer_rsrc_t rv = TV::slab(V, ld, 0, kt * 64);
+#pragma unroll
+    for (int i = 0; i < TK::PER_WAVE; ++i) TK::issue(rk, offk, i, st, wave);
+#pragma unroll
+    for (int i = 0; i < TV::PER_WAVE; ++i) TV::issue(rv, offv, i, st + 8192, wave);
+  };
+#pragma unroll
+  for (int s = 0; s < F64_NST - 1; ++s)
+    if (s < ntiles) issue(s);
+
+  for (int kt = 0; kt < ntiles; ++kt) {
+    wait_slabs<LW, F64_NST - 2>(min(F64_NST - 2, ntiles - 1 - kt));
+    wave_barrier_all();
+    if (kt + F64_NST - 1 < ntiles) issue(kt + F64_NST - 1);
+    const char* ktile = smem + (kt % F64_NST) * F64_STAGE;
+    const char* vtile = ktile + 8192;
+    const int key0 = kt * 64;
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      if (key0 > qg[i] + 31 || qg[i] >= T_) continue;  // every key of the tile is after the group
+      const bool diag = key0 + 63 > qg[i];
+      const int qi = qg[i] + l32;
+      f32x16 sacc[2];
+#pragma unroll
+      for (int js = 0; js < 2; ++js) {
+        sacc[js] = f32x16{};
+#pragma unroll
+        for (int s = 0; s < 4; ++s) Mfma<bf16>::mma(sacc[js], TK::frag(ktile, js * 32, s, lane), qf[i][s]);
+      }
+      float mloc = -INFINITY;
+      if (diag) {
+#pragma unroll
+        for (int js = 0; js < 2; ++js)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const int j = key0 + js * 32 + mfma_row(r, h);
+            if (j > qi) sacc[js][r] = -INFINITY;
+          }
+      }
+#pragma unroll
+      for (int js = 0; js < 2; ++js)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) mloc = fmaxf(mloc, sacc[js][r]);
+      mloc = fmaxf(mloc, __shfl_xor(mloc, 32, 64)) * c;
+      const float m_new = fmaxf(m_run[i], mloc);
+      if (__builtin_amdgcn_ballot_w64(m_new > m_run[i]) != 0) {
+        const float alpha = exp2f(m_run[i] - m_new);
+        o[i][0] *= alpha;
+        o[i][1] *= alpha;
+        l_run[i] *= alpha;
+        m_run[i] = m_new;
+      }
+      u32x4 pb[2][2];
+      float lsum = 0.0f;
+#pragma unroll
+      for (int js = 0; js < 2; ++js) {
+        float p[16];
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          p[r] = exp2f(fmaf(sacc[js][r], c, -m_new));
+          lsum += p[r];
+        }
+#pragma unroll
+        for (int u = 0; u < 2; ++u)
+          pb[js][u] = u32x4{pack_bf16(p[8 * u], p[8 * u + 1]), pack_bf16(p[8 * u + 2], p[8 * u + 3]),
+                            pack_bf16(p[8 * u + 4], p[8 * u + 5]), pack_bf16(p[8 * u + 6], p[8 * u + 7])};
+      }
+      l_run[i] += lsum;
+#pragma unroll
+      for (int js = 0; js < 2; ++js)
+#pragma unroll
+        for (int u = 0; u < 2; ++u)
+#pragma unroll
+          for (int db = 0; db < 2; ++db)
+            Mfma<bf16>::mma(o[i][db], vt_frag(vtile, db * 32, js * 32 + 16 * u, lane), pb[js][u]);
+    }
+  }
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    const int qi = qg[i] + l32;
+    const float l_tot = l_run[i] + __shfl_xor(l_run[i], 32, 64);
+    store_head_row<bf16, 64>(o[i], out + (int64_t)b * T_ * dm + hh * 64, dm, qi, T_, 1.0f / l_tot, h, l32);
+    if (h == 0 && qi < T_) lse[(int64_t)bh * T_ + qi] = (m_run[i] + log2f(l_tot)) * LN2;
+  }
+}
+
 // --------------------------------------------------------------------- backward: D = rowsum
 template <typename T, int HD>
 __global__ void attn_dsum_kernel(const T* __restrict__ out, const T* __restrict__ dout,
@@ -428,6 +589,14 @@ __global__ __launch_bounds__(THREADS) void attn_bwd_dq_kernel(
 
 template <typename T, int HD>
 hipError_t fwd_t(int B, int T_, int H, const void* qkv, void* out, float* lse, hipStream_t s) {
+  if constexpr (sizeof(T) == 2 && HD == 64) {
+    if (T_ % 64 == 0) {
+      dim3 grid((T_ + F64_Q - 1) / F64_Q, B * H);
+      hipLaunchKernelGGL(attn_fwd64_kernel, grid, dim3(THREADS), 0, s, static_cast<const bf16*>(qkv),
+                         static_cast<bf16*>(out), lse, T_, H);
+      return hipGetLastError();
+    }
+  }
   dim3 grid((T_ + 127) / 128, B * H);
   hipLaunchKernelGGL((attn_fwd_kernel<T, HD>), grid, dim3(THREADS), 0, s,
                      static_cast<const T*>(qkv), static_cast<T*>(out), lse, T_, H);
