@@ -161,7 +161,7 @@ gpt2_status gpt2_op_gemm(int32_t precision, int32_t a_kmajor, int32_t b_kmajor, 
  * block; d_out (batch*seq_len, d); d_lse (batch, n_head, seq_len) fp32 natural-log row
  * log-sum-exp of the scaled scores. Element type per precision. gpt2_op_attention_backward
  * takes d_dout (batch*seq_len, d) and writes d_dqkv (batch*seq_len, 3*d); d_scratch must hold
- * batch*n_head*seq_len floats. Asynchronous on hip_stream. */
+ * 2*batch*n_head*seq_len floats. Asynchronous on hip_stream. */
 gpt2_status gpt2_op_attention_forward(int32_t precision, int32_t batch, int32_t seq_len,
                                       int32_t n_head, int32_t head_dim, const void* d_qkv,
                                       void* d_out, float* d_lse, void* hip_stream);

@@ -91,7 +91,7 @@ def _attn_case(torch, prec, B, T, H, hd, seed):
     G.op_attention_forward(g_qkv, g_out, g_lse, B, T, H, hd, precision=prec)
     g_dout = torch.from_numpy(dout).to(tdt).cuda()
     g_dqkv = torch.full((B * T, 3 * d), float("nan"), dtype=tdt, device="cuda")
-    scratch = torch.empty((B * H * T,), dtype=torch.float32, device="cuda")
+    scratch = torch.empty((2 * B * H * T,), dtype=torch.float32, device="cuda")
     G.op_attention_backward(g_qkv, g_out, g_lse, g_dout, g_dqkv, scratch, B, T, H, hd,
                             precision=prec)
     torch.cuda.synchronize()

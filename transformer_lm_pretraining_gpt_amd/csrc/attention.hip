@@ -587,6 +587,281 @@ __global__ __launch_bounds__(THREADS) void attn_bwd_dq_kernel(
                         1.0f / sqrtf((float)HD), h, l32);
 }
 
+// ------------------------------------------------------ backward, bf16 with head_dim 64
+// Head tiles of 64 rows x 64 bf16 ([row][d], 128-byte rows) in LDS, read both as K-major MFMA
+// fragments (rows x d) and transposed (d x rows, ds_read_b64_tr_b16). Chunk c of row r sits at
+// c ^ hswz(r): over 16 consecutive rows the b128 fragment reads cover every bank once, and the
+// four rows x four chunks of a 32-lane transposed read do too (rows r and r+2 land in opposite
+// halves of their 128-byte rows).
+DEV int hswz(int r) { return ((r & 2) << 1) | ((r >> 2) & 3); }
+
+struct HeadTile {
+  static constexpr int PER_WAVE = 2;  // 1 KB wave-loads per tile per wave
+  // per-lane byte offsets (from the tile's first row) of this wave's two loads
+  DEV static void offsets(uint32_t (&off)[2], int64_t ld, int wave, int lane) {
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const int row = (wave * 2 + i) * 8 + lane / 8;
+      off[i] = (uint32_t)(row * ld * 2 + (((lane % 8) ^ hswz(row)) << 4));
+    }
+  }
+  DEV static void issue(__amdgpu_buffer_rsrc_t r, const uint32_t (&off)[2], char* dst, int wave) {
+    lds_dma16(r, off[0], dst + (wave * 2) * 1024);
+    lds_dma16(r, off[1], dst + (wave * 2 + 1) * 1024);
+  }
+  // A fragment: rows rw + l%32, d = 16 s + 8 h .. +7
+  DEV static u32x4 frag(const char* st, int rw, int s, int lane) {
+    const int row = rw + (lane & 31);
+    return *reinterpret_cast<const u32x4*>(st + row * 128 + (((2 * s + (lane >> 5)) ^ hswz(row)) << 4));
+  }
+  // A fragment of the transpose: X^T[d0 + l%32][rows row0 + 4h + 0..3, row0 + 8 + 4h + 0..3], the
+  // row order of registers p[8u .. 8u+7] of an MFMA result (rows mfma_row(r, h)), row0 = 32 b + 16 u
+  DEV static u32x4 tfrag(const char* st, int d0, int row0, int lane) {
+    const int g = lane >> 4, j = lane & 15;
+    const int r = d0 + (g & 1) * 16 + 4 * (j & 3);
+    const int chunk = r >> 3, within = (r & 7) * 2;
+    u32x2 out[2];
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+      const int krow = row0 + 4 * (g >> 1) + 8 * t + (j >> 2);
+      const char* a = st + krow * 128 + ((chunk ^ hswz(krow)) << 4) + within;
+      out[t] = __builtin_bit_cast(
+          u32x2, __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4*)(a)));
+    }
+    return u32x4{out[0][0], out[0][1], out[1][0], out[1][1]};
+  }
+};
+
+DEV u32x4 pack8(const float* p) {
+  return u32x4{pack_bf16(p[0], p[1]), pack_bf16(p[2], p[3]), pack_bf16(p[4], p[5]), pack_bf16(p[6], p[7])};
+}
+
+// Per (batch*head, t): {lse * log2(e), D = sum_d dO O} for the head_dim-64 backward.
+__global__ void attn_dsum64_kernel(const bf16* __restrict__ out, const bf16* __restrict__ dout,
+                                   const float* __restrict__ lse, float2* __restrict__ lsed,
+                                   int T_, int H, int rows) {
+  const int lane = threadIdx.x & 63;
+  const int row = blockIdx.x * (blockDim.x / 64) + (threadIdx.x >> 6);
+  if (row >= rows) return;
+  const int dm = H * 64;
+  const int b = row / T_, t = row % T_;
+  for (int v0 = 0; v0 < dm / 8; v0 += 64) {
+    const int v = v0 + lane;
+    float sum = 0.0f;
+    if (v < dm / 8) {
+      float a[8], g[8];
+      Vec<bf16>::unpack(ld16(out + (int64_t)row * dm + v * 8), a);
+      Vec<bf16>::unpack(ld16(dout + (int64_t)row * dm + v * 8), g);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) sum += a[e] * g[e];
+    }
+#pragma unroll
+    for (int o = 1; o < 8; o <<= 1) sum += __shfl_xor(sum, o, 64);
+    if (v < dm / 8 && (v % 8) == 0) {
+      const int64_t i = ((int64_t)b * H + v / 8) * T_ + t;
+      lsed[i] = make_float2(lse[i] * LOG2E, sum);
+    }
+  }
+}
+
+// dK and dV for 128 keys per block (32 per wave, one key per lane): S = Q K^T and dP = dO V^T
+// with the key's K and V rows as register B operands, then dV^T += dO^T P and dK^T += Q^T dS from
+// the transposed tiles. Query tiles of 64 stream through a three-stage LDS ring with their
+// {lse log2 e, D} pairs.
+constexpr int B64_KEYS = 128;
+constexpr int B64_STAGE = 8192 + 8192 + 512;  // Q tile, dO tile, 64 x float2
+
+__global__ __launch_bounds__(THREADS, 2) void attn_bwd_dkdv64_kernel(
+    const bf16* __restrict__ qkv, const bf16* __restrict__ dout, const float2* __restrict__ lsed,
+    bf16* __restrict__ dqkv, int T_, int H) {
+  constexpr int NST = 3;
+  constexpr int LW = 2 * HeadTile::PER_WAVE + 1;
+  __shared__ __attribute__((aligned(1024))) char smem[NST * B64_STAGE];
+  const int tid = threadIdx.x, lane = tid & 63, h = lane >> 5, l32 = lane & 31;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int bh = blockIdx.y, b = bh / H, hh = bh % H;
+  const int dm = H * 64;
+  const int64_t ld = 3 * (int64_t)dm;
+  const bf16* Q = qkv + (int64_t)b * T_ * ld + hh * 64;
+  const bf16* K = Q + dm;
+  const bf16* V = Q + 2 * dm;
+  const bf16* dO = dout + (int64_t)b * T_ * dm + hh * 64;
+  const float2* lsed_bh = lsed + (int64_t)bh * T_;
+  const int k0 = blockIdx.x * B64_KEYS;  // blocks near the start see the most queries
+  const int kg = k0 + 32 * wave;         // this wave's first key
+  const int kj = kg + l32;               // this lane's key
+  u32x4 kf[4], vf[4];
+  load_row_frags<bf16, 64>(kf, K, ld, kj, T_, h);
+  load_row_frags<bf16, 64>(vf, V, ld, kj, T_, h);
+  f32x16 dk[2], dv[2];
+  dk[0] = dk[1] = dv[0] = dv[1] = f32x16{};
+  const float c = LOG2E / 8.0f;
+
+  const int qt0 = k0 / 64;               // first query tile with a query >= k0
+  const int ntl = T_ / 64 - qt0;
+  uint32_t offq[2], offo[2];
+  HeadTile::offsets(offq, ld, wave, lane);
+  HeadTile::offsets(offo, dm, wave, lane);
+  auto issue = [&](int t) {
+    char* st = smem + (t % NST) * B64_STAGE;
+    const int q = (qt0 + t) * 64;
+    HeadTile::issue(buffer_at(Q + (int64_t)q * ld), offq, st, wave);
+    HeadTile::issue(buffer_at(dO + (int64_t)q * dm), offo, st + 8192, wave);
+    // 16 {lse, D} pairs per wave: lanes 0..7 load two each
+    if (lane < 8) lds_dma16(buffer_at(lsed_bh + q + 16 * wave), (uint32_t)(lane * 16), st + 16384 + wave * 128);
+  };
+#pragma unroll
+  for (int t = 0; t < NST - 1; ++t)
+    if (t < ntl) issue(t);
+
+  for (int t = 0; t < ntl; ++t) {
+    wait_slabs<LW, NST - 2>(min(NST - 2, ntl - 1 - t));
+    wave_barrier_all();
+    if (t + NST - 1 < ntl) issue(t + NST - 1);
+    const char* qt = smem + (t % NST) * B64_STAGE;
+    const char* dot = qt + 8192;
+    const float* ls = reinterpret_cast<const float*>(qt + 16384);
+    const int q = (qt0 + t) * 64;
+#pragma unroll
+    for (int ib = 0; ib < 2; ++ib) {
+      const int iq = q + ib * 32;
+      if (iq + 31 < kg) continue;  // every query of the sub-tile is before this wave's keys
+      const bool diag = iq < kg + 32;
+      f32x16 sacc = f32x16{}, dpacc = f32x16{};
+#pragma unroll
+      for (int s = 0; s < 4; ++s) {
+        Mfma<bf16>::mma(sacc, HeadTile::frag(qt, ib * 32, s, lane), kf[s]);
+        Mfma<bf16>::mma(dpacc, HeadTile::frag(dot, ib * 32, s, lane), vf[s]);
+      }
+      float p[16], ds[16];
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const int il = ib * 32 + g * 8 + h * 4;  // rows mfma_row(4g .. 4g+3, h)
+        const f32x4 a = *reinterpret_cast<const f32x4*>(ls + 2 * il);      // lse0 D0 lse1 D1
+        const f32x4 bb = *reinterpret_cast<const f32x4*>(ls + 2 * il + 4);  // lse2 D2 lse3 D3
+        const float lv[4] = {a[0], a[2], bb[0], bb[2]}, dd[4] = {a[1], a[3], bb[1], bb[3]};
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int r = 4 * g + e;
+          float pr = exp2f(fmaf(sacc[r], c, -lv[e]));
+          if (diag && q + il + e < kj) pr = 0.0f;
+          p[r] = pr;
+          ds[r] = pr * (dpacc[r] - dd[e]);
+        }
+      }
+#pragma unroll
+      for (int u = 0; u < 2; ++u) {
+        const u32x4 pb = pack8(p + 8 * u), dsb = pack8(ds + 8 * u);
+#pragma unroll
+        for (int db = 0; db < 2; ++db) {
+          Mfma<bf16>::mma(dv[db], HeadTile::tfrag(dot, db * 32, ib * 32 + 16 * u, lane), pb);
+          Mfma<bf16>::mma(dk[db], HeadTile::tfrag(qt, db * 32, ib * 32 + 16 * u, lane), dsb);
+        }
+      }
+    }
+  }
+  bf16* dK = dqkv + (int64_t)b * T_ * ld + dm + hh * 64;
+  store_head_row<bf16, 64>(dk, dK, ld, kj, T_, 1.0f / 8.0f, h, l32);
+  store_head_row<bf16, 64>(dv, dK + dm, ld, kj, T_, 1.0f, h, l32);
+}
+
+// dQ for 256 queries per block (wave w: query groups w and 7 - w, one query per lane):
+// S^T = K Q^T and dP^T = V dO^T with the query's Q and dO rows as register B operands, then
+// dQ^T += K^T dS^T from the transposed K tile. Key tiles stream through a three-stage LDS ring.
+__global__ __launch_bounds__(THREADS, 2) void attn_bwd_dq64_kernel(
+    const bf16* __restrict__ qkv, const bf16* __restrict__ dout, const float2* __restrict__ lsed,
+    bf16* __restrict__ dqkv, int T_, int H) {
+  constexpr int NST = 3;
+  constexpr int LW = 2 * HeadTile::PER_WAVE;
+  __shared__ __attribute__((aligned(1024))) char smem[NST * 16384];
+  const int tid = threadIdx.x, lane = tid & 63, h = lane >> 5, l32 = lane & 31;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int nqb = (T_ + F64_Q - 1) / F64_Q;
+  const int qb = nqb - 1 - (int)blockIdx.x;  // heaviest query blocks first
+  const int bh = blockIdx.y, b = bh / H, hh = bh % H;
+  const int dm = H * 64;
+  const int64_t ld = 3 * (int64_t)dm;
+  const bf16* Q = qkv + (int64_t)b * T_ * ld + hh * 64;
+  const bf16* K = Q + dm;
+  const bf16* V = Q + 2 * dm;
+  const bf16* dO = dout + (int64_t)b * T_ * dm + hh * 64;
+  const int q0 = qb * F64_Q;
+  const int ntiles = min(T_, q0 + F64_Q) / 64;
+
+  int qg[2];
+  qg[0] = q0 + 32 * wave;
+  qg[1] = q0 + 32 * (7 - wave);
+  u32x4 qf[2][4], df[2][4];
+  float lse2[2], dsum[2];
+  f32x16 dq[2][2];
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    const int qi = qg[i] + l32;
+    load_row_frags<bf16, 64>(qf[i], Q, ld, qi, T_, h);
+    load_row_frags<bf16, 64>(df[i], dO, dm, qi, T_, h);
+    const float2 v = qi < T_ ? lsed[(int64_t)bh * T_ + qi] : make_float2(0.0f, 0.0f);
+    lse2[i] = v.x;
+    dsum[i] = v.y;
+    dq[i][0] = dq[i][1] = f32x16{};
+  }
+  const float c = LOG2E / 8.0f;
+
+  uint32_t off[2];
+  HeadTile::offsets(off, ld, wave, lane);
+  auto issue = [&](int kt) {
+    char* st = smem + (kt % NST) * 16384;
+    HeadTile::issue(buffer_at(K + (int64_t)kt * 64 * ld), off, st, wave);
+    HeadTile::issue(buffer_at(V + (int64_t)kt * 64 * ld), off, st + 8192, wave);
+  };
+#pragma unroll
+  for (int t = 0; t < NST - 1; ++t)
+    if (t < ntiles) issue(t);
+
+  for (int kt = 0; kt < ntiles; ++kt) {
+    wait_slabs<LW, NST - 2>(min(NST - 2, ntiles - 1 - kt));
+    wave_barrier_all();
+    if (kt + NST - 1 < ntiles) issue(kt + NST - 1);
+    const char* ktile = smem + (kt % NST) * 16384;
+    const char* vtile = ktile + 8192;
+    const int key0 = kt * 64;
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      if (key0 > qg[i] + 31 || qg[i] >= T_) continue;  // every key of the tile is after the group
+      const int qi = qg[i] + l32;
+#pragma unroll
+      for (int js = 0; js < 2; ++js) {
+        const int j0 = key0 + js * 32;
+        if (j0 > qg[i] + 31) continue;
+        const bool diag = j0 + 31 > qg[i];
+        f32x16 sacc = f32x16{}, dpacc = f32x16{};
+#pragma unroll
+        for (int s = 0; s < 4; ++s) {
+          Mfma<bf16>::mma(sacc, HeadTile::frag(ktile, js * 32, s, lane), qf[i][s]);
+          Mfma<bf16>::mma(dpacc, HeadTile::frag(vtile, js * 32, s, lane), df[i][s]);
+        }
+        float ds[16];
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          float pr = exp2f(fmaf(sacc[r], c, -lse2[i]));
+          if (diag && j0 + mfma_row(r, h) > qi) pr = 0.0f;
+          ds[r] = pr * (dpacc[r] - dsum[i]);
+        }
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+          const u32x4 dsb = pack8(ds + 8 * u);
+#pragma unroll
+          for (int db = 0; db < 2; ++db)
+            Mfma<bf16>::mma(dq[i][db], HeadTile::tfrag(ktile, db * 32, js * 32 + 16 * u, lane), dsb);
+        }
+      }
+    }
+  }
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+    store_head_row<bf16, 64>(dq[i], dqkv + (int64_t)b * T_ * ld + hh * 64, ld, qg[i] + l32, T_,
+                             1.0f / 8.0f, h, l32);
+}
+
 template <typename T, int HD>
 hipError_t fwd_t(int B, int T_, int H, const void* qkv, void* out, float* lse, hipStream_t s) {
   if constexpr (sizeof(T) == 2 && HD == 64) {
@@ -607,6 +882,21 @@ template <typename T, int HD>
 hipError_t bwd_t(int B, int T_, int H, const void* qkv, const void* out, const float* lse,
                  const void* dout, void* dqkv, float* dsum, hipStream_t s) {
   const int rows = B * T_;
+  if constexpr (sizeof(T) == 2 && HD == 64) {
+    if (T_ % 64 == 0) {
+      float2* lsed = reinterpret_cast<float2*>(dsum);
+      hipLaunchKernelGGL(attn_dsum64_kernel, dim3((rows + 3) / 4), dim3(256), 0, s,
+                         static_cast<const bf16*>(out), static_cast<const bf16*>(dout), lse, lsed,
+                         T_, H, rows);
+      hipLaunchKernelGGL(attn_bwd_dkdv64_kernel, dim3((T_ + B64_KEYS - 1) / B64_KEYS, B * H),
+                         dim3(THREADS), 0, s, static_cast<const bf16*>(qkv),
+                         static_cast<const bf16*>(dout), lsed, static_cast<bf16*>(dqkv), T_, H);
+      hipLaunchKernelGGL(attn_bwd_dq64_kernel, dim3((T_ + F64_Q - 1) / F64_Q, B * H), dim3(THREADS),
+                         0, s, static_cast<const bf16*>(qkv), static_cast<const bf16*>(dout), lsed,
+                         static_cast<bf16*>(dqkv), T_, H);
+      return hipGetLastError();
+    }
+  }
   hipLaunchKernelGGL((attn_dsum_kernel<T, HD>), dim3((rows + 3) / 4), dim3(256), 0, s,
                      static_cast<const T*>(out), static_cast<const T*>(dout), dsum, T_, H, rows);
   dim3 grid((T_ + 127) / 128, B * H);

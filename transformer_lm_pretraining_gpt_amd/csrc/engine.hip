@@ -242,7 +242,7 @@ size_t carve(const Geo& g, uintptr_t base, Bufs& b) {
   b.dbig = c.take<void>(ts * M * 4 * d);
   b.dqkv = c.take<void>(ts * M * 3 * d);
   b.datt = c.take<void>(ts * M * d);
-  b.dsum = c.take<float>(4 * bht);
+  b.dsum = c.take<float>(8 * bht);  // attention backward scratch: 2 floats per (b, h, t)
   const size_t nblk = (size_t)ln_bwd_blocks(g.M, LN_ROWS_PER_BLOCK);
   const size_t ncs = (M + COLSUM_ROWS_PER_BLOCK - 1) / COLSUM_ROWS_PER_BLOCK;
   b.colpart = c.take<float>(4 * std::max(nblk * 3 * d, ncs * 4 * d));
