@@ -143,7 +143,7 @@ def main():
     lm_flops = lm_work / max(lm_n, 1)
     achieved = lm_flops / (lm_avg_ms / 1e3) / 1e12
     peak_tf = PEAK_BF16_FLOPS / 1e12
-    roof = {"bound": "mfma", "kernel": "LM-head forward GEMM (gemm_dma_kernel<1,1,256,128,64,3,2,1>)",
+    roof = {"bound": "mfma", "kernel": "LM-head forward GEMM (gemm_dma_kernel<1,1,256,256,64,3,1,1,8>)",
             "achieved": round(achieved, 2), "peak": round(peak_tf, 1), "unit": "TFLOP/s",
             "frac": round(achieved / peak_tf, 4), "traffic": _traffic(args.workload),
             "flops_per_launch": lm_flops, "avg_launch_ms": round(lm_avg_ms, 4),

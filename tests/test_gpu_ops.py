@@ -20,9 +20,10 @@ def _stored(torch, logical, kmajor_rows_are_k, dtype):
 
 
 LAYOUTS = [(1, 0), (1, 1), (0, 0), (0, 1)]
-# (6104, 2296, 192): more 128x128 tiles than the chip holds at once, ragged in m and n
+# (6104, 2296, 192): 216 tiles of 256x256 (the 8-wave configuration), ragged in m and n;
+# (4104, 4104, 192): 289 of them, more than the chip holds at once, so blocks loop over tiles
 SHAPES = [(200, 136, 72), (256, 256, 128), (1000, 520, 776), (4096, 2304, 768), (64, 768, 3072),
-          (6104, 2296, 192)]
+          (6104, 2296, 192), (4104, 4104, 192)]
 
 
 @pytest.mark.parametrize("layout", LAYOUTS)

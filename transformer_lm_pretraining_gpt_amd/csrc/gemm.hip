@@ -390,17 +390,19 @@ DEV void slab_mma(f32x16 (&acc)[MB][NB], const char* sa, const char* sb, int wm0
 // (slab count so far) mod NSTAGE across tiles, so when a tile's k loop ends the stage of its last
 // slab is free while the next tile's first NSTAGE-1 slabs go to the others: those loads are issued
 // first and stream in while the finished tile is written out through the free stage.
-template <int AK, int BKM, int BM, int BN, int RB, int NSTAGE, int MINB, int TAG>
-__global__ __launch_bounds__(THREADS, MINB) void gemm_dma_kernel(GemmParams p) {
-  constexpr int WM = BM / 2, WN = BN / 2;
+template <int AK, int BKM, int BM, int BN, int RB, int NSTAGE, int MINB, int TAG, int NW = 4>
+__global__ __launch_bounds__(64 * NW, MINB) void gemm_dma_kernel(GemmParams p) {
+  // NW waves in a 2 x NW/2 grid over the block tile
+  constexpr int WGN = NW / 2;
+  constexpr int WM = BM / 2, WN = BN / WGN;
   constexpr int MB = WM / 32, NB = WN / 32;
   constexpr int KT = RB / 2;
   constexpr int KSTEPS = RB / 32;
   constexpr int STAGE = (BM + BN) * RB;
-  using TA = DmaTile<BM, AK == 1, RB>;
-  using TB = DmaTile<BN, BKM == 1, RB>;
+  using TA = DmaTile<BM, AK == 1, RB, NW>;
+  using TB = DmaTile<BN, BKM == 1, RB, NW>;
   constexpr int LW = TA::PER_WAVE + TB::PER_WAVE;  // loads per wave per slab
-  static_assert(4 * epi_wave_bytes<NB>() <= STAGE, "epilogue buffer must fit one stage");
+  static_assert(NW * epi_wave_bytes<NB>() <= STAGE, "epilogue buffer must fit one stage");
   __shared__ __attribute__((aligned(1024))) char smem[NSTAGE * STAGE];
 
   const int tid = threadIdx.x, lane = tid & 63;
@@ -434,7 +436,7 @@ __global__ __launch_bounds__(THREADS, MINB) void gemm_dma_kernel(GemmParams p) {
 
   const bf16* A = static_cast<const bf16*>(p.A);
   const bf16* B = static_cast<const bf16*>(p.B);
-  const int wm0 = (wave >> 1) * WM, wn0 = (wave & 1) * WN;
+  const int wm0 = (wave / WGN) * WM, wn0 = (wave % WGN) * WN;
 
   // output tile of work item w
   auto tile_origin = [&](int item, int& m0, int& n0) {
@@ -544,44 +546,48 @@ __global__ void splitk_reduce_kernel(const float* __restrict__ part, int splits,
 // Tile configurations of the direct-to-LDS kernel: 256x256 with 128-byte slabs, two stages
 // (128 KB LDS, one block per CU); 256x128 and 128x128 with 64-byte slabs, three stages (72 / 48 KB
 // LDS), two blocks per CU so that one block's epilogue overlaps the other's MFMAs.
-// Blocks of `kernel` resident at once on the current device (CUs x blocks per CU).
+// Blocks of `kernel` (nt threads each) resident at once on the current device.
 template <typename K>
-int resident_blocks(K kernel) {
+int resident_blocks(K kernel, int nt) {
   int dev = 0, cus = 0, per_cu = 0;
   if (hipGetDevice(&dev) != hipSuccess ||
       hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
-      hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kernel, THREADS, 0) != hipSuccess)
+      hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kernel, nt, 0) != hipSuccess)
     return 256;
   return std::max(1, cus * std::max(per_cu, 1));
 }
 
-template <void (*KERNEL)(GemmParams)>
+template <void (*KERNEL)(GemmParams), int NT = THREADS>
 hipError_t launch_persistent(int tiles, int splits, const GemmParams& p, hipStream_t s) {
-  static const int resident = resident_blocks(KERNEL);  // one value per kernel
+  static const int resident = resident_blocks(KERNEL, NT);  // one value per kernel
   const int per_z = std::max(1, resident / splits);
-  dim3 grid(std::min(tiles, per_z), 1, splits), block(THREADS);
+  dim3 grid(std::min(tiles, per_z), 1, splits), block(NT);
   hipLaunchKernelGGL(KERNEL, grid, block, 0, s, p);
   return hipGetLastError();
 }
 
 // Tile configurations of the direct-to-LDS kernel, both with 64-byte slabs (32 k) and three
-// stages: 256x128 (72 KB LDS, two blocks per CU) and 128x128 (48 KB, up to three per CU). With
-// several blocks per CU one block's barriers and epilogue overlap another's MFMAs. Chosen by
-// measurement over the GPT-2 shapes against 256x256 tiles and deeper or shallower pipelines
-// (256x128 for the large products, 128x128 for the rest).
+// stages: 256x256 with 8 waves (wave tiles 128 x 64, two waves per SIMD, 96 KB LDS, one block per
+// CU) and 128x128 with 4 waves (48 KB, up to three blocks per CU). Two waves per SIMD let one
+// wave's barriers and epilogue overlap the other's MFMAs; the large tile issues the fewest loads
+// per MFMA. Chosen by measurement over the GPT-2 shapes against 256x128 tiles with two blocks
+// per CU and deeper or shallower pipelines.
 template <int AK, int BKM, int BM, int BN>
 hipError_t launch_dma(int splits, int tag, const GemmParams& p, hipStream_t s) {
   constexpr int RB = 64;
   constexpr int STAGE = (BM + BN) * RB;
   constexpr int NSTAGE = 3;
-  constexpr int MINB = 2;
+  constexpr int NW = BM == 256 ? 8 : 4;
+  constexpr int MINB = BM == 256 ? 1 : 2;
   static_assert(NSTAGE * STAGE * MINB <= 160 * 1024, "LDS");
   const int tiles = ((p.M + BM - 1) / BM) * ((p.N + BN - 1) / BN);
-  if constexpr (AK == 1 && BKM == 1 && BM == 256 && BN == 128) {
+  if constexpr (AK == 1 && BKM == 1 && BM == 256) {
     if (tag == 1)
-      return launch_persistent<gemm_dma_kernel<AK, BKM, BM, BN, RB, NSTAGE, MINB, 1>>(tiles, splits, p, s);
+      return launch_persistent<gemm_dma_kernel<AK, BKM, BM, BN, RB, NSTAGE, MINB, 1, NW>, 64 * NW>(
+          tiles, splits, p, s);
   }
-  return launch_persistent<gemm_dma_kernel<AK, BKM, BM, BN, RB, NSTAGE, MINB, 0>>(tiles, splits, p, s);
+  return launch_persistent<gemm_dma_kernel<AK, BKM, BM, BN, RB, NSTAGE, MINB, 0, NW>, 64 * NW>(
+      tiles, splits, p, s);
 }
 
 template <typename T, int AK, int BKM, int BM, int BN>
@@ -593,17 +599,15 @@ hipError_t launch_t(int splits, int tag, const GemmParams& p, hipStream_t s) {
         p.N >= (BKM ? 1 : 8) && p.lda < (1 << 22) && p.ldb < (1 << 22))
       return launch_dma<AK, BKM, BM, BN>(splits, tag, p, s);
   }
-  const int tiles = ((p.M + BM - 1) / BM) * ((p.N + BN - 1) / BN);
-  dim3 grid(tiles, 1, splits), block(THREADS);
-  // tag 1: a separately named copy of the LM-head product, so profilers report it on its own
-  if constexpr (sizeof(T) == 2 && AK == 1 && BKM == 1 && BM == 256 && BN == 128) {
-    if (tag == 1) {
-      hipLaunchKernelGGL((gemm_kernel<T, AK, BKM, BM, BN, 1>), grid, block, 0, s, p);
-      return hipGetLastError();
-    }
+  if constexpr (BM != 128 || BN != 128) {
+    // the register-staged kernel runs 128x128 tiles only
+    return launch_t<T, AK, BKM, 128, 128>(splits, tag, p, s);
+  } else {
+    const int tiles = ((p.M + BM - 1) / BM) * ((p.N + BN - 1) / BN);
+    dim3 grid(tiles, 1, splits), block(THREADS);
+    hipLaunchKernelGGL((gemm_kernel<T, AK, BKM, BM, BN, 0>), grid, block, 0, s, p);
+    return hipGetLastError();
   }
-  hipLaunchKernelGGL((gemm_kernel<T, AK, BKM, BM, BN, 0>), grid, block, 0, s, p);
-  return hipGetLastError();
 }
 
 template <typename T, int BM, int BN>
@@ -623,7 +627,7 @@ hipError_t launch_type(int a_kmajor, int b_kmajor, int tile, int splits, int tag
     return launch_layout<T, 128, 128>(a_kmajor, b_kmajor, splits, tag, p, s);
   } else {
     switch (tile) {
-      case TILE_256x128: return launch_layout<T, 256, 128>(a_kmajor, b_kmajor, splits, tag, p, s);
+      case TILE_256: return launch_layout<T, 256, 256>(a_kmajor, b_kmajor, splits, tag, p, s);
       default: return launch_layout<T, 128, 128>(a_kmajor, b_kmajor, splits, tag, p, s);
     }
   }
@@ -635,7 +639,7 @@ int gemm_k_tile(bool is_bf16) { return is_bf16 ? ROWB / 2 : ROWB / 4; }
 
 int gemm_pick_tile(int M, int N) {
   const int64_t t256 = (int64_t)((M + 255) / 256) * ((N + 255) / 256);
-  return t256 >= 512 ? TILE_256x128 : TILE_128;
+  return t256 >= 192 ? TILE_256 : TILE_128;
 }
 
 hipError_t launch_gemm(bool is_bf16, int a_kmajor, int b_kmajor, int tile, int splits, int tag,

@@ -31,7 +31,7 @@ struct GemmParams {
   float alpha, beta;
 };
 
-enum GemmTile { TILE_128 = 0, TILE_256x128 = 2 };
+enum GemmTile { TILE_128 = 0, TILE_256 = 1 };
 
 // Launch C = op(A) op(B) with the given operand layouts (1 = k contiguous). is_bf16 selects the
 // element type of A, B, C(T), C2, aux. splits > 1 requires epi == EPI_F32.

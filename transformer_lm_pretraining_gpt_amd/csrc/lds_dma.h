@@ -77,10 +77,11 @@ DEV int swz_rb(int row) {
 template <int RB>
 DEV int lds_off_rb(int row, int chunk) { return row * RB + ((chunk ^ swz_rb<RB>(row)) << 4); }
 
-template <int R, bool KMAJOR, int RB>
+template <int R, bool KMAJOR, int RB, int NW = 4>
 struct DmaTile {
   static constexpr int KT = RB / 2;                  // k per slab
-  static constexpr int PER_WAVE = R * RB / 4096;     // 1 KB wave-loads per slab per wave
+  static constexpr int PER_WAVE = R * RB / (1024 * NW);  // 1 KB wave-loads per slab per wave
+  static_assert(PER_WAVE >= 1 && PER_WAVE * 1024 * NW == R * RB, "whole wave-loads per wave");
   static constexpr int DS_PER_FRAG = KMAJOR ? 1 : 2;  // LDS read instructions per fragment
   // Byte offsets, relative to the slab origin of the tile starting at row r0, of this wave's
   // loads (one per 1 KB wave-load). They depend on the tile (rows past the matrix are clamped to
