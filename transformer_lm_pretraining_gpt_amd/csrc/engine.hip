@@ -149,12 +149,22 @@ int pick_tile(const Geo& g, int M, int N) {
 // Split of the K = rows reduction of a weight gradient (in x out): about four 128x128 blocks per
 // CU in flight; the fp32 partials are summed by a second kernel in a fixed order.
 struct Split { int splits, k_split; };
+// K splits of a weight-gradient product (in x out, K = tokens). bf16 runs 256x256 tiles at one
+// block per CU, so the splits aim at one round of about 256 blocks (measured best on the GPT-2
+// shapes); fp32 runs 128x128 tiles and aims at about 1024 blocks.
 Split pick_split(const Geo& g, int in, int out) {
   const int kt = 64;
-  const int64_t tiles = (int64_t)((in + 127) / 128) * ((out + 127) / 128);
-  int s = (int)((1024 + tiles - 1) / tiles);
+  int s;
+  if (g.bf16) {
+    const int64_t tiles = (int64_t)((in + 255) / 256) * ((out + 255) / 256);
+    s = (int)(256 / tiles);
+    if (s > 16) s = 16;
+  } else {
+    const int64_t tiles = (int64_t)((in + 127) / 128) * ((out + 127) / 128);
+    s = (int)((1024 + tiles - 1) / tiles);
+    if (s > 8) s = 8;
+  }
   if (s < 1) s = 1;
-  if (s > 8) s = 8;
   int per = (g.M + s - 1) / s;
   per = (per + kt - 1) / kt * kt;
   if (per < kt) per = kt;
@@ -331,12 +341,13 @@ gpt2_status gemm_dw(gpt2_ctx* c, int in, int out, const void* X, const void* dY,
   p.M = in; p.N = out; p.K = g.M; p.k_split = sp.k_split;
   p.epi = EPI_F32; p.alpha = 1.0f;
   Timed t1(c, FAM_GEMM, 2.0 * in * out * g.M);
+  const int tile = g.bf16 ? TILE_256 : TILE_128;
   if (sp.splits == 1) {
     p.C = gw; p.ldc = out; p.beta = accumulate ? 1.0f : 0.0f;
-    HIPCHK(launch_gemm(g.bf16, 0, 0, TILE_128, 1, 0, p, c->stream));
+    HIPCHK(launch_gemm(g.bf16, 0, 0, tile, 1, 0, p, c->stream));
   } else {
     p.C = c->b.splitk; p.ldc = out; p.c_split_stride = (int64_t)in * out; p.beta = 0.0f;
-    HIPCHK(launch_gemm(g.bf16, 0, 0, TILE_128, sp.splits, 0, p, c->stream));
+    HIPCHK(launch_gemm(g.bf16, 0, 0, tile, sp.splits, 0, p, c->stream));
     HIPCHK(launch_splitk_reduce(c->b.splitk, sp.splits, (int64_t)in * out, in, out, gw, out, 1.0f,
                                 accumulate ? 1.0f : 0.0f, c->stream));
   }
