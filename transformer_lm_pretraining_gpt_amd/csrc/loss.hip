@@ -5,7 +5,7 @@
 // uma RTX 4090", section "Configuração do treinamento"); the padded columns are masked out: they
 // take no part in the log-sum-exp and receive zero gradient.
 //
-// One block per row reads the row once into registers (16-byte vectors), forms the max, the sum
+// One block of 1024 threads per row reads the row once into registers (16-byte vectors), forms the max, the sum
 // of exponentials and the log-sum-exp, writes the per-row loss lse - z[y], and overwrites the row
 // in place with softmax(z) - onehot(y) (zeros in the padded columns). The 1/M mean and the
 // backward's grad_scale are applied later, as the alpha of the LM-head gradient products, so no
@@ -17,8 +17,8 @@
 
 namespace {
 
-constexpr int THREADS = 512;
-constexpr int MAXV = 16;  // 16-byte vectors per thread held in registers
+constexpr int THREADS = 1024;
+constexpr int MAXV = 8;   // 16-byte vectors per thread held in registers
 constexpr float LOG2E = 1.4426950408889634f;
 
 DEV float block_reduce(float v, float* sh, bool is_max) {
@@ -32,16 +32,42 @@ DEV float block_reduce(float v, float* sh, bool is_max) {
   return r;
 }
 
+// Elements j0 + e >= V of a loaded vector set to -inf (padded vocabulary columns), so that they
+// drop out of the max and every exponential without a test per element.
 template <typename T>
-__global__ __launch_bounds__(THREADS) void xent_kernel(int V, int Vp, T* __restrict__ logits,
-                                                       const int32_t* __restrict__ targets,
-                                                       float* __restrict__ row_loss,
-                                                       int* __restrict__ err) {
+DEV u32x4 mask_tail(u32x4 r, int j0, int V) {
+  if constexpr (sizeof(T) == 2) {
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+      if (j0 + 2 * w >= V) r[w] = (r[w] & 0xffff0000u) | 0xff80u;
+      if (j0 + 2 * w + 1 >= V) r[w] = (r[w] & 0x0000ffffu) | 0xff800000u;
+    }
+  } else {
+#pragma unroll
+    for (int w = 0; w < 4; ++w)
+      if (j0 + w >= V) r[w] = 0xff800000u;
+  }
+  return r;
+}
+
+// Hide the packed registers from the optimizer between passes: unpacking again is cheap, while
+// keeping every unpacked float alive across passes would cost the occupancy this kernel needs.
+DEV void opaque(u32x4 (&reg)[MAXV]) {
+#pragma unroll
+  for (int k = 0; k < MAXV; ++k) asm volatile("" : "+v"(reg[k]));
+}
+
+template <typename T>
+__global__ __launch_bounds__(THREADS, 8) void xent_kernel(int V, int Vp, T* __restrict__ logits,
+                                                          const int32_t* __restrict__ targets,
+                                                          float* __restrict__ row_loss,
+                                                          int* __restrict__ err) {
   constexpr int VE = 16 / (int)sizeof(T);
   __shared__ float sh[THREADS / 64];
   const int row = blockIdx.x, tid = threadIdx.x;
   T* z = logits + (int64_t)row * Vp;
   const int nvec = Vp / VE;
+  const int nfull = V / VE;  // vectors with no padded column
   int y = targets[row];
   if (y < 0 || y >= V) {
     if (tid == 0) atomicOr(err, ERR_TARGET_RANGE);
@@ -54,14 +80,16 @@ __global__ __launch_bounds__(THREADS) void xent_kernel(int V, int Vp, T* __restr
     const int v = tid + k * THREADS;
     if (v < nvec) {
       reg[k] = ld16(z + v * VE);
+      if (v >= nfull) reg[k] = mask_tail<T>(reg[k], v * VE, V);
       float f[VE];
       Vec<T>::unpack(reg[k], f);
 #pragma unroll
-      for (int e = 0; e < VE; ++e)
-        if (v * VE + e < V) mx = fmaxf(mx, f[e]);
+      for (int e = 0; e < VE; ++e) mx = fmaxf(mx, f[e]);
     }
   }
+  opaque(reg);
   mx = block_reduce(mx, sh, true);
+  const float mx2 = mx * LOG2E;
   float sum = 0.0f;
 #pragma unroll
   for (int k = 0; k < MAXV; ++k) {
@@ -70,14 +98,17 @@ __global__ __launch_bounds__(THREADS) void xent_kernel(int V, int Vp, T* __restr
       float f[VE];
       Vec<T>::unpack(reg[k], f);
 #pragma unroll
-      for (int e = 0; e < VE; ++e)
-        if (v * VE + e < V) sum += exp2f((f[e] - mx) * LOG2E);
+      for (int e = 0; e < VE; ++e) sum += exp2f(fmaf(f[e], LOG2E, -mx2));
     }
   }
+  opaque(reg);
   sum = block_reduce(sum, sh, false);
   const float lse = mx + logf(sum);
+  const float lse2 = lse * LOG2E;
   if (tid == 0) row_loss[row] = lse - to_f32(z[y]);
   __syncthreads();  // z[y] is read before any thread overwrites the row
+  // softmax(z) - onehot(y); padded columns give exp2(-inf) = 0
+  const int vy = y / VE, ey = y % VE;
 #pragma unroll
   for (int k = 0; k < MAXV; ++k) {
     const int v = tid + k * THREADS;
@@ -85,9 +116,11 @@ __global__ __launch_bounds__(THREADS) void xent_kernel(int V, int Vp, T* __restr
       float f[VE];
       Vec<T>::unpack(reg[k], f);
 #pragma unroll
-      for (int e = 0; e < VE; ++e) {
-        const int j = v * VE + e;
-        f[e] = j < V ? exp2f((f[e] - lse) * LOG2E) - (j == y ? 1.0f : 0.0f) : 0.0f;
+      for (int e = 0; e < VE; ++e) f[e] = exp2f(fmaf(f[e], LOG2E, -lse2));
+      if (v == vy) {
+#pragma unroll
+        for (int e = 0; e < VE; ++e)
+          if (e == ey) f[e] -= 1.0f;
       }
       st16(z + v * VE, Vec<T>::pack(f));
     }
