@@ -9,6 +9,8 @@
 //   db = sum_rows dy.
 // Column sums never use atomics: each block writes its partial row, a second kernel adds the
 // partials in a fixed order, so results are bitwise reproducible.
+#include <type_traits>
+
 #include "common.h"
 #include "kernels.h"
 
@@ -26,7 +28,7 @@ DEV void store4(T* dst, const float (&v)[4]) {
                     __builtin_bit_cast(uint32_t, v[2]), __builtin_bit_cast(uint32_t, v[3])});
 }
 
-template <typename T>
+template <typename T, int NV>
 __global__ __launch_bounds__(256) void ln_fwd_kernel(int M, int d, const float* __restrict__ x,
                                                      const float* __restrict__ g,
                                                      const float* __restrict__ b,
@@ -37,10 +39,10 @@ __global__ __launch_bounds__(256) void ln_fwd_kernel(int M, int d, const float* 
   if (row >= M) return;
   const int nv = d >> 2;
   const float* xr = x + (int64_t)row * d;
-  f32x4 xv[MAXV];
+  f32x4 xv[NV];
   float s = 0.0f;
 #pragma unroll
-  for (int k = 0; k < MAXV; ++k) {
+  for (int k = 0; k < NV; ++k) {
     const int v = lane + 64 * k;
     xv[k] = v < nv ? *reinterpret_cast<const f32x4*>(xr + 4 * v) : f32x4{0, 0, 0, 0};
     s += (xv[k][0] + xv[k][1]) + (xv[k][2] + xv[k][3]);
@@ -48,7 +50,7 @@ __global__ __launch_bounds__(256) void ln_fwd_kernel(int M, int d, const float* 
   const float mu = wave_sum(s) / (float)d;
   float s2 = 0.0f;
 #pragma unroll
-  for (int k = 0; k < MAXV; ++k) {
+  for (int k = 0; k < NV; ++k) {
     const int v = lane + 64 * k;
     if (v < nv) {
 #pragma unroll
@@ -61,7 +63,7 @@ __global__ __launch_bounds__(256) void ln_fwd_kernel(int M, int d, const float* 
   const float var = wave_sum(s2) / (float)d;
   const float r = 1.0f / sqrtf(var + LN_EPS);
 #pragma unroll
-  for (int k = 0; k < MAXV; ++k) {
+  for (int k = 0; k < NV; ++k) {
     const int v = lane + 64 * k;
     if (v < nv) {
       const f32x4 gv = *reinterpret_cast<const f32x4*>(g + 4 * v);
@@ -79,7 +81,7 @@ __global__ __launch_bounds__(256) void ln_fwd_kernel(int M, int d, const float* 
 }
 
 // One block = 4 waves over rows [blk*rpb, blk*rpb + rpb); wave w takes rows w, w+4, ...
-template <typename T>
+template <typename T, int NV>
 __global__ __launch_bounds__(256) void ln_bwd_kernel(
     int M, int d, const float* __restrict__ dy, const float* __restrict__ x,
     const float* __restrict__ mean, const float* __restrict__ rstd, const float* __restrict__ g,
@@ -88,9 +90,9 @@ __global__ __launch_bounds__(256) void ln_bwd_kernel(
   extern __shared__ float red[];  // [4][d]
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int nv = d >> 2;
-  f32x4 pg[MAXV], pb[MAXV], pr[MAXV], gv[MAXV];
+  f32x4 pg[NV], pb[NV], pr[NV], gv[NV];
 #pragma unroll
-  for (int k = 0; k < MAXV; ++k) {
+  for (int k = 0; k < NV; ++k) {
     pg[k] = pb[k] = pr[k] = f32x4{0, 0, 0, 0};
     const int v = lane + 64 * k;
     gv[k] = v < nv ? *reinterpret_cast<const f32x4*>(g + 4 * v) : f32x4{0, 0, 0, 0};
@@ -99,14 +101,16 @@ __global__ __launch_bounds__(256) void ln_bwd_kernel(
   for (int row = r0 + wave; row < r1; row += 4) {
     const float mu = mean[row], rs = rstd[row];
     const int64_t base = (int64_t)row * d;
-    f32x4 xh[MAXV], dyv[MAXV];
+    f32x4 xh[NV], dyv[NV], dr[NV];
     float s1 = 0.0f, s2 = 0.0f;
 #pragma unroll
-    for (int k = 0; k < MAXV; ++k) {
+    for (int k = 0; k < NV; ++k) {
       const int v = lane + 64 * k;
       if (v < nv) {
         const f32x4 xv = *reinterpret_cast<const f32x4*>(x + base + 4 * v);
         dyv[k] = *reinterpret_cast<const f32x4*>(dy + base + 4 * v);
+        // the incoming residual gradient is loaded with the row, ahead of the reductions
+        dr[k] = has_dres ? *reinterpret_cast<const f32x4*>(dres + base + 4 * v) : f32x4{0, 0, 0, 0};
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           xh[k][e] = (xv[e] - mu) * rs;
@@ -119,11 +123,10 @@ __global__ __launch_bounds__(256) void ln_bwd_kernel(
     s1 = wave_sum(s1) / (float)d;
     s2 = wave_sum(s2) / (float)d;
 #pragma unroll
-    for (int k = 0; k < MAXV; ++k) {
+    for (int k = 0; k < NV; ++k) {
       const int v = lane + 64 * k;
       if (v < nv) {
-        f32x4 nw = has_dres ? *reinterpret_cast<const f32x4*>(dres + base + 4 * v)
-                            : f32x4{0, 0, 0, 0};
+        f32x4 nw = dr[k];
         float o[4];
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
@@ -144,7 +147,7 @@ __global__ __launch_bounds__(256) void ln_bwd_kernel(
 #pragma unroll
   for (int kind = 0; kind < 3; ++kind) {
 #pragma unroll
-    for (int k = 0; k < MAXV; ++k) {
+    for (int k = 0; k < NV; ++k) {
       const int v = lane + 64 * k;
       if (v < nv)
         *reinterpret_cast<f32x4*>(red + wave * d + 4 * v) =
@@ -221,18 +224,40 @@ __global__ __launch_bounds__(64 * RED_WAVES) void colsum_reduce_kernel(
 
 }  // namespace
 
+namespace {
+// Calls f(std::integral_constant<int, NV>) with NV = float4 vectors per lane for rows of d floats
+// (1 .. MAXV), so that the per-lane arrays are sized for the actual width.
+template <typename F>
+hipError_t with_nv(int d, F&& f) {
+  switch ((d / 4 + 63) / 64) {
+    case 1: return f(std::integral_constant<int, 1>{});
+    case 2: return f(std::integral_constant<int, 2>{});
+    case 3: return f(std::integral_constant<int, 3>{});
+    case 4: return f(std::integral_constant<int, 4>{});
+    case 5: return f(std::integral_constant<int, 5>{});
+    case 6: return f(std::integral_constant<int, 6>{});
+    case 7: return f(std::integral_constant<int, 7>{});
+    case 8: return f(std::integral_constant<int, 8>{});
+  }
+  return hipErrorInvalidValue;
+}
+}  // namespace
+
 hipError_t launch_ln_fwd(bool is_bf16, int M, int d, const float* x, const float* g,
                          const float* b, void* y, float* mean, float* rstd, hipStream_t s) {
   if (M == 0) return hipSuccess;
   if (d % 4 || d > 4 * 64 * MAXV) return hipErrorInvalidValue;
   dim3 grid((M + 3) / 4);
-  if (is_bf16)
-    hipLaunchKernelGGL(ln_fwd_kernel<bf16>, grid, dim3(256), 0, s, M, d, x, g, b,
-                       static_cast<bf16*>(y), mean, rstd);
-  else
-    hipLaunchKernelGGL(ln_fwd_kernel<float>, grid, dim3(256), 0, s, M, d, x, g, b,
-                       static_cast<float*>(y), mean, rstd);
-  return hipGetLastError();
+  return with_nv(d, [&](auto nv) {
+    constexpr int NV = decltype(nv)::value;
+    if (is_bf16)
+      hipLaunchKernelGGL((ln_fwd_kernel<bf16, NV>), grid, dim3(256), 0, s, M, d, x, g, b,
+                         static_cast<bf16*>(y), mean, rstd);
+    else
+      hipLaunchKernelGGL((ln_fwd_kernel<float, NV>), grid, dim3(256), 0, s, M, d, x, g, b,
+                         static_cast<float*>(y), mean, rstd);
+    return hipGetLastError();
+  });
 }
 
 int ln_bwd_blocks(int M, int rows_per_block) { return (M + rows_per_block - 1) / rows_per_block; }
@@ -245,13 +270,16 @@ hipError_t launch_ln_bwd(bool is_bf16, int M, int d, const float* dy, const floa
   if (d % 4 || d > 4 * 64 * MAXV) return hipErrorInvalidValue;
   dim3 grid(ln_bwd_blocks(M, rows_per_block));
   const size_t lds = 4 * (size_t)d * sizeof(float);
-  if (is_bf16)
-    hipLaunchKernelGGL(ln_bwd_kernel<bf16>, grid, dim3(256), lds, s, M, d, dy, x, mean, rstd, g,
-                       dres, has_dres, static_cast<bf16*>(dres_t), part, rows_per_block);
-  else
-    hipLaunchKernelGGL(ln_bwd_kernel<float>, grid, dim3(256), lds, s, M, d, dy, x, mean, rstd, g,
-                       dres, has_dres, static_cast<float*>(dres_t), part, rows_per_block);
-  return hipGetLastError();
+  return with_nv(d, [&](auto nv) {
+    constexpr int NV = decltype(nv)::value;
+    if (is_bf16)
+      hipLaunchKernelGGL((ln_bwd_kernel<bf16, NV>), grid, dim3(256), lds, s, M, d, dy, x, mean, rstd,
+                         g, dres, has_dres, static_cast<bf16*>(dres_t), part, rows_per_block);
+    else
+      hipLaunchKernelGGL((ln_bwd_kernel<float, NV>), grid, dim3(256), lds, s, M, d, dy, x, mean, rstd,
+                         g, dres, has_dres, static_cast<float*>(dres_t), part, rows_per_block);
+    return hipGetLastError();
+  });
 }
 
 hipError_t launch_colsum_partial(bool src_bf16, int M, int N, const void* src, int64_t ld,
