@@ -27,7 +27,7 @@ TRAFFIC_FILE = os.path.join(ROOT, "profiles", "lm_head_gemm_traffic.json")
 
 def _source_hash() -> str:
     h = hashlib.sha256()
-    for f in ("gemm.hip", "common.h", "kernels.h"):
+    for f in ("gemm.hip", "lds_dma.h", "common.h", "kernels.h"):
         with open(os.path.join(ROOT, "transformer_lm_pretraining_gpt_amd", "csrc", f), "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()[:16]
@@ -80,6 +80,9 @@ def main():
     ap.add_argument("--workload", default="gpt2_124m")
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle's cpu_baseline leg")
     ap.add_argument("--no-breakdown", action="store_true", help="skip per-family kernel timing")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="also run one plain elementwise copy of 1 GiB (read 1 GiB, write 1 GiB): "
+                         "the reference dispatch that scales HBM byte counters")
     args = ap.parse_args()
     if args.gpus != 1:
         print(json.dumps({"error": "this build runs on exactly one GPU; --gpus must be 1",
@@ -185,6 +188,15 @@ def main():
                              "achieved": round(rate / 1e9, 1), "unit": unit,
                              "frac": round(rate / 1e9 / HBM_PEAK_GBS, 4)}
         out["kernels"] = fams
+
+    if args.copy_calibration:
+        src = torch.ones(1 << 28, dtype=torch.float32, device="cuda")
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        torch.mul(src, 1.0, out=dst)
+        torch.cuda.synchronize()
+        out["copy_calibration_bytes"] = {"read": 1 << 30, "write": 1 << 30}
+        del src, dst
 
     if not args.no_cpu:
         x0, y0 = S.batch_from_stream(stream, B, T, 0)
