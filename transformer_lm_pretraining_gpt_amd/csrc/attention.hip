@@ -238,11 +238,11 @@ __global__ __launch_bounds__(THREADS) void attn_fwd_kernel(const T* __restrict__
       }
       mloc = fmaxf(mloc, __shfl_xor(mloc, 32, 64));
       const float m_new = fmaxf(m_run, mloc);
-      const float alpha = exp2f(m_run - m_new);
+      const float alpha = fast_exp2(m_run - m_new);
       float lsum = 0.0f;
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        p[r] = exp2f(p[r] - m_new);
+        p[r] = fast_exp2(p[r] - m_new);
         lsum += p[r];
       }
       l_run = l_run * alpha + lsum;
@@ -377,7 +377,7 @@ __global__ __launch_bounds__(THREADS, 2) void attn_fwd64_kernel(const bf16* __re
       mloc = fmaxf(mloc, __shfl_xor(mloc, 32, 64)) * c;
       const float m_new = fmaxf(m_run[i], mloc);
       if (__builtin_amdgcn_ballot_w64(m_new > m_run[i]) != 0) {
-        const float alpha = exp2f(m_run[i] - m_new);
+        const float alpha = fast_exp2(m_run[i] - m_new);
         o[i][0] *= alpha;
         o[i][1] *= alpha;
         l_run[i] *= alpha;
@@ -390,7 +390,7 @@ __global__ __launch_bounds__(THREADS, 2) void attn_fwd64_kernel(const bf16* __re
         float p[16];
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-          p[r] = exp2f(fmaf(sacc[js][r], c, -m_new));
+          p[r] = fast_exp2(fmaf(sacc[js][r], c, -m_new));
           lsum += p[r];
         }
 #pragma unroll
@@ -512,7 +512,7 @@ __global__ __launch_bounds__(THREADS) void attn_bwd_dkdv_kernel(
         for (int e = 0; e < 4; ++e) {
           const int r = 4 * g + e;
           const int i = i0 + il + e;
-          const float pr = (i < kj || i >= T_) ? 0.0f : exp2f(s[r] * c - lv[e]);
+          const float pr = (i < kj || i >= T_) ? 0.0f : fast_exp2(s[r] * c - lv[e]);
           p[r] = pr;
           ds[r] = pr * (dp[r] - dd[e]);
         }
@@ -577,7 +577,7 @@ __global__ __launch_bounds__(THREADS) void attn_bwd_dq_kernel(
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         const int j = j0 + mfma_row(r, h);
-        const float pr = (j > qi || j >= T_) ? 0.0f : exp2f(s[r] * c - lse_i);
+        const float pr = (j > qi || j >= T_) ? 0.0f : fast_exp2(s[r] * c - lse_i);
         ds[r] = pr * (dp[r] - d_i);
       }
       mma_transposed<T, HD>(dq, kt, jb * 32, ds, h, l32);
@@ -743,7 +743,7 @@ __global__ __launch_bounds__(THREADS, 2) void attn_bwd_dkdv64_kernel(
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           const int r = 4 * g + e;
-          float pr = exp2f(fmaf(sacc[r], c, -lv[e]));
+          float pr = fast_exp2(fmaf(sacc[r], c, -lv[e]));
           if (diag && q + il + e < kj) pr = 0.0f;
           p[r] = pr;
           ds[r] = pr * (dpacc[r] - dd[e]);
@@ -842,7 +842,7 @@ __global__ __launch_bounds__(THREADS, 2) void attn_bwd_dq64_kernel(
         float ds[16];
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-          float pr = exp2f(fmaf(sacc[r], c, -lse2[i]));
+          float pr = fast_exp2(fmaf(sacc[r], c, -lse2[i]));
           if (diag && j0 + mfma_row(r, h) > qi) pr = 0.0f;
           ds[r] = pr * (dpacc[r] - dsum[i]);
         }

@@ -26,9 +26,17 @@ template <> DEV bf16 from_f32<bf16>(float x) { return (bf16)x; }
 DEV uint32_t bf16_bits(bf16 x) { return (uint32_t)__builtin_bit_cast(uint16_t, x); }
 DEV float bf16lo(uint32_t w) { return __builtin_bit_cast(float, w << 16); }
 DEV float bf16hi(uint32_t w) { return __builtin_bit_cast(float, w & 0xffff0000u); }
+typedef __attribute__((ext_vector_type(2))) float f32x2;
+typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2;
+// Two floats to two bf16 (round to nearest even) in one v_cvt_pk_bf16_f32, lo in bits 0..15.
 DEV uint32_t pack_bf16(float lo, float hi) {
-  return bf16_bits((bf16)lo) | (bf16_bits((bf16)hi) << 16);
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{lo, hi}, bf16x2));
 }
+
+// 2^x with the bare v_exp_f32 (about 1 ulp, as exp2f). exp2f adds a range check and rescaling
+// around it so that results below 2^-126 stay exact denormals; softmax and cross-entropy do not
+// need those (they add nothing to a sum dominated by the maximum term), so the hot loops skip it.
+DEV float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
 // ---------------------------------------------------------------------------------------------
 // Elements per 16-byte vector, and unpack/pack of one 16-byte vector into floats.

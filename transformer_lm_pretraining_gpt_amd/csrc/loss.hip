@@ -98,7 +98,7 @@ __global__ __launch_bounds__(THREADS, 8) void xent_kernel(int V, int Vp, T* __re
       float f[VE];
       Vec<T>::unpack(reg[k], f);
 #pragma unroll
-      for (int e = 0; e < VE; ++e) sum += exp2f(fmaf(f[e], LOG2E, -mx2));
+      for (int e = 0; e < VE; ++e) sum += fast_exp2(fmaf(f[e], LOG2E, -mx2));
     }
   }
   opaque(reg);
@@ -116,7 +116,7 @@ __global__ __launch_bounds__(THREADS, 8) void xent_kernel(int V, int Vp, T* __re
       float f[VE];
       Vec<T>::unpack(reg[k], f);
 #pragma unroll
-      for (int e = 0; e < VE; ++e) f[e] = exp2f(fmaf(f[e], LOG2E, -lse2));
+      for (int e = 0; e < VE; ++e) f[e] = fast_exp2(fmaf(f[e], LOG2E, -lse2));
       if (v == vy) {
 #pragma unroll
         for (int e = 0; e < VE; ++e)
