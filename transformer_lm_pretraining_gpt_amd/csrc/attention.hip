@@ -17,6 +17,8 @@
 //   dV = P^T dO,  dP = dO V^T,  dS = P o (dP - D),  dQ = dS K / sqrt(hd),  dK = dS^T Q / sqrt(hd).
 #include <math.h>
 
+#include <type_traits>
+
 #include "common.h"
 #include "kernels.h"
 #include "lds_dma.h"
@@ -341,11 +343,14 @@ __global__ __launch_bounds__(THREADS, 2) void attn_fwd64_kernel(const bf16* __re
   for (int s = 0; s < F64_NST - 1; ++s)
     if (s < ntiles) issue(s);
 
-  for (int kt = 0; kt < ntiles; ++kt) {
+// the tile loop is unrolled over the three stages so that each stage's LDS offset is a
+  // compile-time constant (folded into the LDS instructions' offsets)
+  auto tile = [&](auto stc, int kt) {
+    constexpr int ST = decltype(stc)::value;
     wait_slabs<LW, F64_NST - 2>(min(F64_NST - 2, ntiles - 1 - kt));
     wave_barrier_all();
     if (kt + F64_NST - 1 < ntiles) issue(kt + F64_NST - 1);
-    const char* ktile = smem + (kt % F64_NST) * F64_STAGE;
+    const char* ktile = smem + ST * F64_STAGE;
     const char* vtile = ktile + 8192;
     const int key0 = kt * 64;
 #pragma unroll
@@ -407,6 +412,11 @@ __global__ __launch_bounds__(THREADS, 2) void attn_fwd64_kernel(const bf16* __re
           for (int db = 0; db < 2; ++db)
             Mfma<bf16>::mma(o[i][db], vt_frag(vtile, db * 32, js * 32 + 16 * u, lane), pb[js][u]);
     }
+    };
+  for (int kt0 = 0; kt0 < ntiles; kt0 += 3) {
+    tile(std::integral_constant<int, 0>{}, kt0);
+    if (kt0 + 1 < ntiles) tile(std::integral_constant<int, 1>{}, kt0 + 1);
+    if (kt0 + 2 < ntiles) tile(std::integral_constant<int, 2>{}, kt0 + 2);
   }
 #pragma unroll
   for (int i = 0; i < 2; ++i) {
@@ -714,11 +724,14 @@ __global__ __launch_bounds__(THREADS, 2) void attn_bwd_dkdv64_kernel(
   for (int t = 0; t < NST - 1; ++t)
     if (t < ntl) issue(t);
 
-  for (int t = 0; t < ntl; ++t) {
+// the tile loop is unrolled over the three stages so that each stage's LDS offset is a
+  // compile-time constant (folded into the LDS instructions' offsets)
+  auto tile = [&](auto stc, int t) {
+    constexpr int ST = decltype(stc)::value;
     wait_slabs<LW, NST - 2>(min(NST - 2, ntl - 1 - t));
     wave_barrier_all();
     if (t + NST - 1 < ntl) issue(t + NST - 1);
-    const char* qt = smem + (t % NST) * B64_STAGE;
+    const char* qt = smem + ST * B64_STAGE;
     const char* dot = qt + 8192;
     const float* ls = reinterpret_cast<const float*>(qt + 16384);
     const int q = (qt0 + t) * 64;
@@ -759,6 +772,11 @@ __global__ __launch_bounds__(THREADS, 2) void attn_bwd_dkdv64_kernel(
         }
       }
     }
+    };
+  for (int t0 = 0; t0 < ntl; t0 += 3) {
+    tile(std::integral_constant<int, 0>{}, t0);
+    if (t0 + 1 < ntl) tile(std::integral_constant<int, 1>{}, t0 + 1);
+    if (t0 + 2 < ntl) tile(std::integral_constant<int, 2>{}, t0 + 2);
   }
   bf16* dK = dqkv + (int64_t)b * T_ * ld + dm + hh * 64;
   store_head_row<bf16, 64>(dk, dK, ld, kj, T_, 1.0f / 8.0f, h, l32);
@@ -817,11 +835,14 @@ __global__ __launch_bounds__(THREADS, 2) void attn_bwd_dq64_kernel(
   for (int t = 0; t < NST - 1; ++t)
     if (t < ntiles) issue(t);
 
-  for (int kt = 0; kt < ntiles; ++kt) {
+// the tile loop is unrolled over the three stages so that each stage's LDS offset is a
+  // compile-time constant (folded into the LDS instructions' offsets)
+  auto tile = [&](auto stc, int kt) {
+    constexpr int ST = decltype(stc)::value;
     wait_slabs<LW, NST - 2>(min(NST - 2, ntiles - 1 - kt));
     wave_barrier_all();
     if (kt + NST - 1 < ntiles) issue(kt + NST - 1);
-    const char* ktile = smem + (kt % NST) * 16384;
+    const char* ktile = smem + ST * 16384;
     const char* vtile = ktile + 8192;
     const int key0 = kt * 64;
 #pragma unroll
@@ -855,6 +876,11 @@ __global__ __launch_bounds__(THREADS, 2) void attn_bwd_dq64_kernel(
         }
       }
     }
+    };
+  for (int kt0 = 0; kt0 < ntiles; kt0 += 3) {
+    tile(std::integral_constant<int, 0>{}, kt0);
+    if (kt0 + 1 < ntiles) tile(std::integral_constant<int, 1>{}, kt0 + 1);
+    if (kt0 + 2 < ntiles) tile(std::integral_constant<int, 2>{}, kt0 + 2);
   }
 #pragma unroll
   for (int i = 0; i < 2; ++i)
