@@ -275,6 +275,73 @@ constexpr int epi_pitch() { return NB * 32 + 8; }
 template <int NB>
 constexpr int epi_wave_bytes() { return 8 * epi_pitch<NB>() * 4; }
 
+// bf16-output epilogue (plain store with alpha and bias, or bias + GELU with both outputs) for
+// 64-column wave tiles. The arithmetic runs in the MFMA register layout (a lane's column is fixed
+// within an accumulator tile, so its bias is one value), the results are converted to bf16 there
+// and written as 16-bit values into the wave's 4 KB LDS buffer, 32 rows at a time; each lane then
+// reads one 16-byte chunk of a row and stores it. Rows are 128 bytes with chunk c at
+// c ^ 4((row/4) mod 2): the two lane halves write rows four apart into opposite halves of the row,
+// and the 16-lane groups of the b128 reads cover all banks.
+DEV int epi16_swz(int row) { return ((row >> 2) & 1) << 2; }
+DEV int epi16_off(int row, int col) {  // byte offset of element (row, col) of a 32 x 64 tile
+  return row * 128 + (((col >> 3) ^ epi16_swz(row)) << 4) + (col & 7) * 2;
+}
+
+template <int EPI, int MB, int NB>
+DEV void epilogue_bf16(const f32x16 (&acc)[MB][NB], const GemmParams& p, char* buf, int row0,
+                       int col0, int lane) {
+  static_assert(NB == 2, "64-column wave tiles");
+  const int h = lane >> 5, l32 = lane & 31;
+  float bias[NB];
+#pragma unroll
+  for (int j = 0; j < NB; ++j) {
+    const int col = col0 + j * 32 + l32;
+    bias[j] = (p.bias && col < p.N) ? p.bias[col] : 0.0f;
+  }
+  constexpr int NOUT = EPI == EPI_BIAS_GELU ? 2 : 1;
+#pragma unroll
+  for (int i = 0; i < MB; ++i) {
+#pragma unroll
+    for (int out = 0; out < NOUT; ++out) {
+      // 32 rows x 64 columns of this output into LDS
+#pragma unroll
+      for (int j = 0; j < NB; ++j)
+#pragma unroll
+        for (int r = 0; r < 16; r += 2) {
+          float x0, x1;
+          if constexpr (EPI == EPI_STORE) {
+            x0 = p.alpha * acc[i][j][r] + bias[j];
+            x1 = p.alpha * acc[i][j][r + 1] + bias[j];
+          } else {
+            x0 = acc[i][j][r] + bias[j];
+            x1 = acc[i][j][r + 1] + bias[j];
+            if (out == 1) {
+              x0 = gelu_tanh(x0);
+              x1 = gelu_tanh(x1);
+            }
+          }
+          const uint32_t pk = pack_bf16(x0, x1);
+          const int rr = mfma_row(r, h), col = j * 32 + l32;  // rows rr and rr + 1
+          *reinterpret_cast<uint16_t*>(buf + epi16_off(rr, col)) = (uint16_t)pk;
+          *reinterpret_cast<uint16_t*>(buf + epi16_off(rr + 1, col)) = (uint16_t)(pk >> 16);
+        }
+      __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0): this wave's LDS writes are done
+      asm volatile("" ::: "memory");
+      bf16* dst = static_cast<bf16*>(out == 0 ? p.C : p.C2);
+#pragma unroll
+      for (int pass = 0; pass < 4; ++pass) {
+        const int rl = pass * 8 + lane / 8, pos = lane % 8;
+        const u32x4 v = *reinterpret_cast<const u32x4*>(buf + rl * 128 + pos * 16);
+        const int row = row0 + i * 32 + rl;
+        const int col = col0 + ((pos ^ epi16_swz(rl)) << 3);
+        if (row < p.M && col < p.N) st16(dst + (int64_t)row * p.ldc + col, v);
+      }
+      __builtin_amdgcn_s_waitcnt(0xc07f);
+      asm volatile("" ::: "memory");
+    }
+  }
+}
+
 template <int EPI, int MB, int NB>
 DEV void epilogue_rows(const f32x16 (&acc)[MB][NB], const GemmParams& p, float* buf, int row0,
                        int col0, int lane) {
@@ -515,9 +582,11 @@ __global__ __launch_bounds__(64 * NW, MINB) void gemm_dma_kernel(GemmParams p) {
     }
     float* buf = reinterpret_cast<float*>(smem + last * STAGE + wave * epi_wave_bytes<NB>());
     const int row0 = m0 + wm0, col0 = n0 + wn0;
+    char* buf16 = smem + last * STAGE + wave * 4096;
+    static_assert(NW * 4096 <= STAGE, "bf16 epilogue buffers must fit one stage");
     switch (p.epi) {
-      case EPI_STORE: epilogue_rows<EPI_STORE, MB, NB>(acc, p, buf, row0, col0, lane); break;
-      case EPI_BIAS_GELU: epilogue_rows<EPI_BIAS_GELU, MB, NB>(acc, p, buf, row0, col0, lane); break;
+      case EPI_STORE: epilogue_bf16<EPI_STORE, MB, NB>(acc, p, buf16, row0, col0, lane); break;
+      case EPI_BIAS_GELU: epilogue_bf16<EPI_BIAS_GELU, MB, NB>(acc, p, buf16, row0, col0, lane); break;
       case EPI_BIAS_RESID: epilogue_rows<EPI_BIAS_RESID, MB, NB>(acc, p, buf, row0, col0, lane); break;
       case EPI_GELU_BWD: epilogue_rows<EPI_GELU_BWD, MB, NB>(acc, p, buf, row0, col0, lane); break;
       default: epilogue_rows<EPI_F32, MB, NB>(acc, p, buf, row0, col0, lane); break;
