@@ -599,6 +599,8 @@ __global__ __launch_bounds__(64 * NW, MINB) void gemm_dma_kernel(GemmParams p) {
   }
 }
 
+// C = alpha * (sum of the K-split partials, in split order) + beta * C. The order is fixed, so the
+// result does not depend on scheduling.
 __global__ void splitk_reduce_kernel(const float* __restrict__ part, int splits, int64_t stride,
                                      int M, int N, float* __restrict__ C, int64_t ldc, float alpha,
                                      float beta) {
@@ -612,9 +614,30 @@ __global__ void splitk_reduce_kernel(const float* __restrict__ part, int splits,
   C[src] = alpha * s + prev;
 }
 
-// Tile configurations of the direct-to-LDS kernel: 256x256 with 128-byte slabs, two stages
-// (128 KB LDS, one block per CU); 256x128 and 128x128 with 64-byte slabs, three stages (72 / 48 KB
-// LDS), two blocks per CU so that one block's epilogue overlaps the other's MFMAs.
+// The same with four columns per thread (N, ldc and stride multiples of 4, 16-byte aligned).
+__global__ void splitk_reduce4_kernel(const float* __restrict__ part, int splits, int64_t stride,
+                                      int M, int N, float* __restrict__ C, int64_t ldc,
+                                      float alpha, float beta) {
+  const int nv = N / 4;
+  const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (idx >= (int64_t)M * nv) return;
+  const int row = (int)(idx / nv), c4 = (int)(idx % nv);
+  const int64_t src = (int64_t)row * ldc + 4 * c4;
+  f32x4 s = f32x4{0, 0, 0, 0};
+  int z = 0;
+  for (; z + 4 <= splits; z += 4) {  // four loads in flight, still added in split order
+    const f32x4 a = *reinterpret_cast<const f32x4*>(part + (int64_t)z * stride + src);
+    const f32x4 b = *reinterpret_cast<const f32x4*>(part + (int64_t)(z + 1) * stride + src);
+    const f32x4 c = *reinterpret_cast<const f32x4*>(part + (int64_t)(z + 2) * stride + src);
+    const f32x4 d = *reinterpret_cast<const f32x4*>(part + (int64_t)(z + 3) * stride + src);
+    s = (((s + a) + b) + c) + d;
+  }
+  for (; z < splits; ++z) s += *reinterpret_cast<const f32x4*>(part + (int64_t)z * stride + src);
+  f32x4* out = reinterpret_cast<f32x4*>(C + src);
+  const f32x4 prev = beta != 0.0f ? beta * *out : f32x4{0, 0, 0, 0};
+  *out = alpha * s + prev;
+}
+
 // Blocks of `kernel` (nt threads each) resident at once on the current device.
 template <typename K>
 int resident_blocks(K kernel, int nt) {
@@ -722,7 +745,15 @@ hipError_t launch_splitk_reduce(const float* part, int splits, int64_t split_str
                                 float* C, int64_t ldc, float alpha, float beta, hipStream_t s) {
   const int64_t n = (int64_t)M * N;
   if (n == 0) return hipSuccess;
-  hipLaunchKernelGGL(splitk_reduce_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s,
-                     part, splits, split_stride, M, N, C, ldc, alpha, beta);
+  const bool vec = N % 4 == 0 && ldc % 4 == 0 && split_stride % 4 == 0 &&
+                   reinterpret_cast<uintptr_t>(part) % 16 == 0 && reinterpret_cast<uintptr_t>(C) % 16 == 0;
+  if (vec) {
+    const int64_t n4 = n / 4;
+    hipLaunchKernelGGL(splitk_reduce4_kernel, dim3((unsigned)((n4 + 255) / 256)), dim3(256), 0, s,
+                       part, splits, split_stride, M, N, C, ldc, alpha, beta);
+  } else {
+    hipLaunchKernelGGL(splitk_reduce_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s,
+                       part, splits, split_stride, M, N, C, ldc, alpha, beta);
+  }
   return hipGetLastError();
 }
