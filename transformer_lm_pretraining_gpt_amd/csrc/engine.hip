@@ -141,17 +141,20 @@ std::vector<AdamSeg> decay_segments(const Geo& g) {
 // ------------------------------------------------------------------------------ GEMM plans
 // Tile choice measured on the GPT-2 shapes: 256x256 tiles only when they still give at least two
 // rounds of blocks over the 256 CUs; otherwise 128x128 tiles (several blocks per CU).
+// The GELU-backward product also sums its output columns when it takes the direct-to-LDS bf16
+// path (K = d a multiple of 64, leading dimensions well inside 32-bit offsets).
+bool fused_colsum(const Geo& g) { return g.bf16 && g.d % 64 == 0 && 4 * g.d < (1 << 22); }
+
 int pick_tile(const Geo& g, int M, int N) {
   if (!g.bf16) return TILE_128;
   return gemm_pick_tile(M, N);
 }
 
-// Split of the K = rows reduction of a weight gradient (in x out): about four 128x128 blocks per
-// CU in flight; the fp32 partials are summed by a second kernel in a fixed order.
+// Split of the K = rows reduction of a weight gradient (in x out, K = tokens); the fp32 partials
+// are summed by a second kernel in a fixed order. bf16 runs 256x256 tiles at one block per CU, so
+// the splits aim at one round of about 256 blocks (measured best on the GPT-2 shapes); fp32 runs
+// 128x128 tiles and aims at about 1024 blocks.
 struct Split { int splits, k_split; };
-// K splits of a weight-gradient product (in x out, K = tokens). bf16 runs 256x256 tiles at one
-// block per CU, so the splits aim at one round of about 256 blocks (measured best on the GPT-2
-// shapes); fp32 runs 128x128 tiles and aims at about 1024 blocks.
 Split pick_split(const Geo& g, int in, int out) {
   const int kt = 64;
   int s;
@@ -317,12 +320,14 @@ const void* W(gpt2_ctx* c, int64_t off) {
 gpt2_status gemm(gpt2_ctx* c, int a_kmajor, int b_kmajor, int M, int N, int K, const void* A,
                  int64_t lda, const void* B, int64_t ldb, int epi, void* C, int64_t ldc,
                  const float* bias = nullptr, const float* resid = nullptr, void* C2 = nullptr,
-                 const void* aux = nullptr, float alpha = 1.0f, float beta = 0.0f, int tag = 0) {
+                 const void* aux = nullptr, float alpha = 1.0f, float beta = 0.0f, int tag = 0,
+                 float* colsum = nullptr) {
   GemmParams p{};
   p.A = A; p.lda = lda; p.B = B; p.ldb = ldb;
   p.M = M; p.N = N; p.K = K; p.k_split = K;
   p.epi = epi; p.C = C; p.ldc = ldc; p.c_split_stride = 0;
   p.C2 = C2; p.bias = bias; p.resid = resid; p.aux = aux; p.alpha = alpha; p.beta = beta;
+  p.colsum = colsum;
   const double fl = 2.0 * M * N * K;
   Timed t1(c, FAM_GEMM, fl);
   Timed t0(c, tag == 1 ? FAM_LMHEAD : -2, fl);
@@ -446,9 +451,20 @@ gpt2_status backward(gpt2_ctx* c, float grad_scale, int acc) {
   for (int l = g.L - 1; l >= 0; --l) {
     // h_{l+1} = h_mid + act W_proj + b_proj ; dres holds dh_{l+1}
     STEP(gemm_dw(c, 4 * d, d, b.act[l], b.dres_t, G + g.wproj(l), acc));
-    STEP(gemm(c, 1, 1, M, 4 * d, d, b.dres_t, d, W(c, g.wproj(l)), d, EPI_GELU_BWD, b.dbig, 4 * d,
-              nullptr, nullptr, nullptr, b.fc[l]));
-    STEP(colsum(c, b.dbig, 4 * d, G + g.bfc(l), acc));
+    // du = (dh W_proj^T) o GELU'(u); its column sums (the fc bias gradient) come out of the same
+    // product's epilogue as one partial row per 128 (or 64) rows when it runs the direct-to-LDS
+    // bf16 path, else from a separate pass
+    if (fused_colsum(g)) {
+      const int bm = pick_tile(g, M, 4 * d) == TILE_256 ? 256 : 128;
+      STEP(gemm(c, 1, 1, M, 4 * d, d, b.dres_t, d, W(c, g.wproj(l)), d, EPI_GELU_BWD, b.dbig,
+                4 * d, nullptr, nullptr, nullptr, b.fc[l], 1.0f, 0.0f, 0, b.colpart));
+      HIPCHK(launch_colsum_reduce(b.colpart, 2 * ((M + bm - 1) / bm), 4 * d, 4 * d, G + g.bfc(l),
+                                  acc, c->stream));
+    } else {
+      STEP(gemm(c, 1, 1, M, 4 * d, d, b.dres_t, d, W(c, g.wproj(l)), d, EPI_GELU_BWD, b.dbig,
+                4 * d, nullptr, nullptr, nullptr, b.fc[l]));
+      STEP(colsum(c, b.dbig, 4 * d, G + g.bfc(l), acc));
+    }
     STEP(gemm_dw(c, d, 4 * d, b.ln2[l], b.dbig, G + g.wfc(l), acc));
     STEP(gemm(c, 1, 1, M, d, 4 * d, b.dbig, 4 * d, W(c, g.wfc(l)), 4 * d, EPI_F32, b.dtmp, d));
     STEP(ln_backward(c, b.resid_mid[l], b.ln2_mean[l], b.ln2_rstd[l], g.ln2g(l), g.ln2b(l),

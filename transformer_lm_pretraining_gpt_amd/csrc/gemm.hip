@@ -352,6 +352,7 @@ DEV void epilogue_rows(const f32x16 (&acc)[MB][NB], const GemmParams& p, float* 
   const int h = lane >> 5, l32 = lane & 31;
   float* cf = static_cast<float*>(p.C);
   if (EPI == EPI_F32) cf += (int64_t)blockIdx.z * p.c_split_stride;
+  float csum[4] = {0.0f, 0.0f, 0.0f, 0.0f};  // EPI_GELU_BWD column sums of this lane's 4 columns
 #pragma unroll
   for (int i = 0; i < MB; ++i) {
 #pragma unroll
@@ -393,7 +394,10 @@ DEV void epilogue_rows(const f32x16 (&acc)[MB][NB], const GemmParams& p, float* 
             const u32x2 u = ld8(static_cast<const bf16*>(p.aux) + o);
             const float uf[4] = {bf16lo(u[0]), bf16hi(u[0]), bf16lo(u[1]), bf16hi(u[1])};
 #pragma unroll
-            for (int e = 0; e < 4; ++e) out[e] = v[e] * gelu_tanh_grad(uf[e]);
+            for (int e = 0; e < 4; ++e) {
+              out[e] = v[e] * gelu_tanh_grad(uf[e]);
+              csum[e] += out[e];
+            }
             st8(static_cast<bf16*>(p.C) + o, u32x2{pack_bf16(out[0], out[1]), pack_bf16(out[2], out[3])});
           } else {
             f32x4 prev = f32x4{0, 0, 0, 0};
@@ -404,6 +408,21 @@ DEV void epilogue_rows(const f32x16 (&acc)[MB][NB], const GemmParams& p, float* 
       }
       __builtin_amdgcn_s_waitcnt(0xc07f);
       asm volatile("" ::: "memory");
+    }
+  }
+  if constexpr (EPI == EPI_GELU_BWD) {
+    if (p.colsum) {
+      // lanes c4, c4 + V4, ... hold the same columns: add them in a fixed order, then lanes
+      // 0 .. V4-1 write the wave's partial row for its WM-row block
+#pragma unroll
+      for (int sh = V4; sh < 64; sh <<= 1)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) csum[e] += __shfl_xor(csum[e], sh, 64);
+      const int col = col0 + (lane % V4) * 4;
+      if (lane < V4 && col < p.N) {
+        float* dst = p.colsum + (int64_t)(row0 / (MB * 32)) * p.N + col;
+        *reinterpret_cast<f32x4*>(dst) = f32x4{csum[0], csum[1], csum[2], csum[3]};
+      }
     }
   }
 }

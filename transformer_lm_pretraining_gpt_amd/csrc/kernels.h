@@ -29,6 +29,9 @@ struct GemmParams {
   const float* resid;
   const void* aux;
   float alpha, beta;
+  // EPI_GELU_BWD on the direct-to-LDS path only: when set, column sums of the output over each
+  // 128-row block of a wave tile go to colsum[(row / 128) * N + col] (fp32, before rounding)
+  float* colsum;
 };
 
 enum GemmTile { TILE_128 = 0, TILE_256 = 1 };

@@ -48,11 +48,13 @@ class GPT2Error(RuntimeError):
 _lib = None
 
 
-def load_library(path: str = LIB_PATH):
-    """Load libgpt2.so (after torch, so that both share one HIP runtime) and declare signatures."""
+def load_library(path: str | None = None):
+    """Load libgpt2.so (after torch, so that both share one HIP runtime) and declare signatures.
+    The library is the in-tree build unless GPT2_LIBRARY names another build of it."""
     global _lib
     if _lib is not None:
         return _lib
+    path = path or os.environ.get("GPT2_LIBRARY") or LIB_PATH
     if not os.path.exists(path):
         raise RuntimeError(f"{path} is not built; run: python -m transformer_lm_pretraining_gpt_amd.build")
     try:
