@@ -56,6 +56,23 @@ DEV void wait_slabs(int after) {
     else wait_slabs<LW, A - 1>(after);
   }
 }
+// vmcnt(N) and lgkmcnt(0) in one wait (this wave's LDS reads have returned)
+template <int N>
+DEV void wait_vmcnt_lgkm0() {
+  static_assert(N >= 0 && N < 64, "vmcnt");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4));
+  asm volatile("" ::: "memory");
+}
+template <int LW, int A>
+DEV void wait_slabs_lgkm0(int after) {
+  if constexpr (A == 0) {
+    wait_vmcnt_lgkm0<0>();
+  } else {
+    if (after >= A) wait_vmcnt_lgkm0<A * LW>();
+    else wait_slabs_lgkm0<LW, A - 1>(after);
+  }
+}
+
 // Chunk swizzle of a tile stored k-row by k-row with R columns (2R bytes, R/8 chunks per k-row).
 // A 32-lane half of ds_read_b64_tr_b16 reads 4 consecutive k-rows x 4 chunks: with k-rows of 256
 // bytes or more all four rows share one 256-byte bank window, so their chunks are XORed with
