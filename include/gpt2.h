@@ -156,6 +156,28 @@ gpt2_status gpt2_op_gemm(int32_t precision, int32_t a_kmajor, int32_t b_kmajor, 
                          int64_t ldb, float* d_c, int64_t ldc, float alpha, float beta,
                          void* hip_stream);
 
+/* The same product with one of the step's fused epilogues, on the kernel and tile the step uses
+ * for an (m, n) output ([6ND]; the GELU is the tanh form of GPT-2's MLP, [CFG]). bf16 A and B,
+ * laid out as for gpt2_op_gemm, fp32 accumulation of Y = A B; then, per element (i, j):
+ *   GPT2_EPI_STORE      C bf16 = bf16(alpha * Y + bias[j])
+ *   GPT2_EPI_BIAS_GELU  C bf16 = bf16(u), C2 bf16 = bf16(gelu(u)), u = Y + bias[j]   (alpha unused)
+ *   GPT2_EPI_BIAS_RESID C fp32 = aux[i, j] + Y + bias[j], aux fp32                     (alpha unused)
+ *   GPT2_EPI_GELU_BWD   C bf16 = bf16(Y * gelu'(aux[i, j])), aux bf16, bias unused  (alpha unused)
+ * where gelu(u) = u/2 (1 + tanh(sqrt(2/pi) (u + 0.044715 u^3))). C, C2 and aux share the row
+ * pitch ldc (elements); d_bias holds n floats or is NULL (zero). n and ldc must be multiples of
+ * 8 and every pointer 16-byte aligned (GPT2_E_UNSUPPORTED otherwise). Asynchronous on hip_stream. */
+typedef enum {
+  GPT2_EPI_STORE = 0,
+  GPT2_EPI_BIAS_GELU = 1,
+  GPT2_EPI_BIAS_RESID = 2,
+  GPT2_EPI_GELU_BWD = 3
+} gpt2_epilogue;
+gpt2_status gpt2_op_gemm_epilogue(int32_t a_kmajor, int32_t b_kmajor, int32_t m, int32_t n,
+                                  int32_t k, const void* d_a, int64_t lda, const void* d_b,
+                                  int64_t ldb, int32_t epilogue, void* d_c, void* d_c2,
+                                  int64_t ldc, const float* d_bias, const void* d_aux, float alpha,
+                                  void* hip_stream);
+
 /* Causal multi-head attention on the step's kernels ([ATT]). d_qkv is (batch*seq_len, 3*d) with
  * q, k, v in column blocks [0,d), [d,2d), [2d,3d) and head h in columns h*hd..h*hd+hd-1 of each
  * block; d_out (batch*seq_len, d); d_lse (batch, n_head, seq_len) fp32 natural-log row

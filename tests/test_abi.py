@@ -104,6 +104,13 @@ def test_null_context_and_ops_are_rejected(lib):
     assert lib.gpt2_destroy(None) == G.GPT2_E_INVALID
     assert lib.gpt2_op_gemm(1, 1, 1, 8, 8, 8, None, 8, None, 8, None, 8, 1.0, 0.0, None) == G.GPT2_E_INVALID
     assert lib.gpt2_op_gemm(1, 1, 1, 8, 8, 12, 16, 12, 16, 12, 16, 8, 1.0, 0.0, None) == G.GPT2_E_UNSUPPORTED
+    epi = lib.gpt2_op_gemm_epilogue
+    assert epi(1, 1, 8, 8, 8, None, 8, None, 8, 0, None, None, 8, None, None, 1.0, None) == G.GPT2_E_INVALID
+    assert epi(1, 1, 8, 8, 8, 16, 8, 16, 8, 7, 16, None, 8, None, None, 1.0, None) == G.GPT2_E_INVALID
+    assert epi(1, 1, 8, 8, 8, 16, 8, 16, 8, 1, 16, None, 8, None, None, 1.0, None) == G.GPT2_E_INVALID
+    assert epi(1, 1, 8, 8, 8, 16, 8, 16, 8, 2, 16, None, 8, None, None, 1.0, None) == G.GPT2_E_INVALID
+    assert epi(1, 1, 8, 12, 8, 16, 8, 16, 8, 0, 16, None, 16, None, None, 1.0, None) == G.GPT2_E_UNSUPPORTED
+    assert epi(1, 1, 8, 8, 8, 16, 8, 24, 8, 0, 16, None, 8, None, None, 1.0, None) == G.GPT2_E_UNSUPPORTED
     assert lib.gpt2_op_attention_forward(1, 1, 8, 1, 48, 16, 16, 16, None) == G.GPT2_E_UNSUPPORTED
     pc = ctypes.c_size_t()
     assert lib.gpt2_param_count(None, ctypes.byref(pc)) == G.GPT2_E_INVALID

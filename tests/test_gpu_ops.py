@@ -22,8 +22,10 @@ def _stored(torch, logical, kmajor_rows_are_k, dtype):
 LAYOUTS = [(1, 0), (1, 1), (0, 0), (0, 1)]
 # (6104, 2296, 192): 216 tiles of 256x256 (the 8-wave configuration), ragged in m and n;
 # (4104, 4104, 192): 289 of them, more than the chip holds at once, so blocks loop over tiles
+# (16296, 768, 192) and (10000, 1152, 128): 192 and 200 tiles of 256x256 with n a multiple of 384,
+# which k-major A runs as 256 and 237 tiles of 128x384, ragged in m
 SHAPES = [(200, 136, 72), (256, 256, 128), (1000, 520, 776), (4096, 2304, 768), (64, 768, 3072),
-          (6104, 2296, 192), (4104, 4104, 192)]
+          (6104, 2296, 192), (4104, 4104, 192), (16296, 768, 192), (10000, 1152, 128)]
 
 
 @pytest.mark.parametrize("layout", LAYOUTS)
@@ -42,6 +44,79 @@ def test_gemm_bf16_exact_integers(layout, shape):
     torch.cuda.synchronize()
     ref = (a.astype(np.float64) @ b.astype(np.float64)).astype(np.float32)
     assert np.array_equal(c.cpu().numpy(), ref)
+
+
+def _gelu(u):
+    return 0.5 * u * (1.0 + np.tanh(math.sqrt(2.0 / math.pi) * (u + 0.044715 * u ** 3)))
+
+
+def _gelu_grad(u):
+    c = math.sqrt(2.0 / math.pi)
+    t = np.tanh(c * (u + 0.044715 * u ** 3))
+    return 0.5 * (1.0 + t) + 0.5 * u * (1.0 - t * t) * c * (1.0 + 3.0 * 0.044715 * u * u)
+
+
+def _bf16_round(torch, x):
+    """float64 values -> the nearest bf16 (via the exact fp32 value), back as float64."""
+    return torch.from_numpy(np.asarray(x, np.float32)).to(torch.bfloat16).to(torch.float64).numpy()
+
+
+# (shape, layout): the register-staged kernel (k not a multiple of 64), the 128x128 and 256x256
+# direct-to-LDS tiles, and the 128x384 tile with either B layout and 2 or 3 column tiles
+EPI_CASES = [((200, 136, 72), (1, 0)), ((1000, 520, 768), (1, 1)), ((1000, 520, 768), (0, 0)),
+             ((6104, 2296, 192), (1, 0)), ((16296, 768, 192), (1, 0)), ((16296, 768, 192), (1, 1)),
+             ((10000, 1152, 128), (1, 1))]
+
+
+@pytest.mark.parametrize("epi", [G.EPI_STORE, G.EPI_BIAS_GELU, G.EPI_BIAS_RESID, G.EPI_GELU_BWD])
+@pytest.mark.parametrize("case", EPI_CASES)
+def test_gemm_fused_epilogues(case, epi):
+    """The step's fused GEMM epilogues. Inputs are multiples of 1/8 (bf16-exact) whose products
+    and sums, and the bias and residual terms, are exact in fp32: the linear outputs must match
+    the float64 reference rounded once to the output type, bit for bit; the GELU forms are
+    compared within one bf16 ulp plus 1e-6 (the kernel's fp32 tanh form against float64, where
+    1 + tanh cancels for negative arguments)."""
+    torch = torch_cuda()
+    (m, n, k), (ak, bk) = case
+    rng = np.random.default_rng(m + 3 * n + 7 * k + 101 * epi + 11 * ak + 5 * bk)
+    a = rng.integers(-1, 2, size=(m, k)).astype(np.float64) / 8
+    b = rng.integers(-1, 2, size=(k, n)).astype(np.float64) / 8
+    bias = rng.integers(-16, 17, size=n).astype(np.float64) / 8
+    y = a @ b
+    da = _stored(torch, a, ak == 1, torch.bfloat16)
+    db = _stored(torch, b.T, bk == 1, torch.bfloat16)
+    dbias = torch.from_numpy(bias.astype(np.float32)).cuda()
+    out_f32 = epi == G.EPI_BIAS_RESID
+    c = torch.full((m, n), float("nan"), dtype=torch.float32 if out_f32 else torch.bfloat16,
+                   device="cuda")
+    c2 = aux = None
+    alpha = 1.0
+    if epi == G.EPI_STORE:
+        alpha = 0.5
+        want = _bf16_round(torch, alpha * y + bias)
+    elif epi == G.EPI_BIAS_GELU:
+        c2 = torch.full_like(c, float("nan"))
+        want = _bf16_round(torch, y + bias)
+        want2 = _gelu(y + bias)
+    elif epi == G.EPI_BIAS_RESID:
+        resid = rng.integers(-64, 65, size=(m, n)).astype(np.float64) / 8
+        aux = torch.from_numpy(resid.astype(np.float32)).cuda()
+        want = resid + y + bias
+    else:
+        u = _bf16_round(torch, rng.normal(0.0, 2.0, size=(m, n)))
+        aux = torch.from_numpy(u.astype(np.float32)).to(torch.bfloat16).cuda()
+        want = y * _gelu_grad(u)
+    G.op_gemm_epilogue(da, db, c, a_kmajor=ak, b_kmajor=bk, m=m, n=n, k=k, epilogue=epi, c2=c2,
+                       bias=None if epi == G.EPI_GELU_BWD else dbias, aux=aux, alpha=alpha)
+    torch.cuda.synchronize()
+    got = c.to(torch.float64).cpu().numpy()
+    if epi == G.EPI_GELU_BWD:
+        assert np.all(np.abs(got - want) <= 2 ** -7 * np.abs(want) + 1e-6)
+    else:
+        assert np.array_equal(got, want)
+    if epi == G.EPI_BIAS_GELU:
+        got2 = c2.to(torch.float64).cpu().numpy()
+        assert np.all(np.abs(got2 - want2) <= 2 ** -7 * np.abs(want2) + 1e-6)
 
 
 def test_gemm_bf16_lm_head_shape_exact():

@@ -721,6 +721,41 @@ gpt2_status gpt2_op_gemm(int32_t precision, int32_t a_kmajor, int32_t b_kmajor, 
   return GPT2_OK;
 }
 
+static_assert(GPT2_EPI_STORE == EPI_STORE && GPT2_EPI_BIAS_GELU == EPI_BIAS_GELU &&
+                  GPT2_EPI_BIAS_RESID == EPI_BIAS_RESID && GPT2_EPI_GELU_BWD == EPI_GELU_BWD,
+              "ABI epilogue codes");
+
+gpt2_status gpt2_op_gemm_epilogue(int32_t a_kmajor, int32_t b_kmajor, int32_t m, int32_t n,
+                                  int32_t k, const void* d_a, int64_t lda, const void* d_b,
+                                  int64_t ldb, int32_t epilogue, void* d_c, void* d_c2,
+                                  int64_t ldc, const float* d_bias, const void* d_aux, float alpha,
+                                  void* hip_stream) {
+  if (m < 0 || n < 0 || k < 0) return fail(GPT2_E_INVALID, "negative size");
+  if (epilogue < GPT2_EPI_STORE || epilogue > GPT2_EPI_GELU_BWD) return fail(GPT2_E_INVALID, "epilogue");
+  const bool needs_c2 = epilogue == GPT2_EPI_BIAS_GELU;
+  const bool needs_aux = epilogue == GPT2_EPI_BIAS_RESID || epilogue == GPT2_EPI_GELU_BWD;
+  if (!d_a || !d_b || !d_c || (needs_c2 && !d_c2) || (needs_aux && !d_aux))
+    return fail(GPT2_E_INVALID, "NULL operand");
+  const int a_row = a_kmajor ? k : m, b_row = b_kmajor ? k : n;
+  if (lda < a_row || ldb < b_row || ldc < n) return fail(GPT2_E_INVALID, "leading dimension too small");
+  if (a_row % 8 || b_row % 8 || lda % 8 || ldb % 8 || n % 8 || ldc % 8)
+    return fail(GPT2_E_UNSUPPORTED, "row lengths, n and leading dimensions must be multiples of 8");
+  const void* ptrs[] = {d_a, d_b, d_c, d_c2, d_bias, d_aux};
+  for (const void* q : ptrs)
+    if (reinterpret_cast<uintptr_t>(q) % 16) return fail(GPT2_E_UNSUPPORTED, "pointers must be 16-byte aligned");
+  GemmParams p{};
+  p.A = d_a; p.lda = lda; p.B = d_b; p.ldb = ldb; p.M = m; p.N = n; p.K = k; p.k_split = k;
+  p.epi = epilogue;  // the internal codes of these four epilogues are the ABI's
+  p.C = d_c; p.C2 = d_c2; p.ldc = ldc; p.bias = epilogue == GPT2_EPI_GELU_BWD ? nullptr : d_bias;
+  p.resid = epilogue == GPT2_EPI_BIAS_RESID ? static_cast<const float*>(d_aux) : nullptr;
+  p.aux = epilogue == GPT2_EPI_GELU_BWD ? d_aux : nullptr;
+  p.alpha = epilogue == GPT2_EPI_STORE ? alpha : 1.0f;
+  p.beta = 0.0f;
+  HIPCHK(launch_gemm(true, a_kmajor ? 1 : 0, b_kmajor ? 1 : 0, gemm_pick_tile(m, n), 1, 0, p,
+                     static_cast<hipStream_t>(hip_stream)));
+  return GPT2_OK;
+}
+
 static gpt2_status attn_args(int32_t precision, int32_t batch, int32_t seq_len, int32_t n_head,
                              int32_t head_dim) {
   if (precision != GPT2_FP32 && precision != GPT2_BF16) return fail(GPT2_E_INVALID, "precision");

@@ -354,7 +354,8 @@ DEV void epilogue_rows(const f32x16 (&acc)[MB][NB], const GemmParams& p, float* 
   constexpr int WN = NB * 32;
   constexpr int PITCH = epi_pitch<NB>();
   constexpr int V4 = WN / 4;     // float4 per row
-  constexpr int RPP = 64 / V4;   // rows per pass
+  constexpr int RPP = 64 / V4;   // rows per pass (lanes from RPP * V4 on idle when V4 is 24)
+  static_assert(8 % RPP == 0, "whole passes over the 8 rows");
   const int h = lane >> 5, l32 = lane & 31;
   float* cf = static_cast<float*>(p.C);
   if (EPI == EPI_F32) cf += (int64_t)blockIdx.z * p.c_split_stride;
@@ -371,6 +372,7 @@ DEV void epilogue_rows(const f32x16 (&acc)[MB][NB], const GemmParams& p, float* 
       asm volatile("" ::: "memory");
 #pragma unroll
       for (int pass = 0; pass < 8 / RPP; ++pass) {
+        if (RPP * V4 < 64 && lane >= RPP * V4) continue;
         const int rl = pass * RPP + lane / V4;
         const int c4 = lane % V4;
         const int row = row0 + i * 32 + 8 * q + rl;
@@ -416,7 +418,7 @@ DEV void epilogue_rows(const f32x16 (&acc)[MB][NB], const GemmParams& p, float* 
       asm volatile("" ::: "memory");
     }
   }
-  if constexpr (EPI == EPI_GELU_BWD) {
+  if constexpr (EPI == EPI_GELU_BWD && 64 % V4 == 0) {  // not with 96-column wave tiles
     if (p.colsum) {
       // lanes c4, c4 + V4, ... hold the same columns: add them in a fixed order, then lanes
       // 0 .. V4-1 write the wave's partial row for its WM-row block
@@ -725,10 +727,12 @@ __global__ __launch_bounds__(64 * NW, MINB) void gemm_dma_kernel(GemmParams p) {
     static_assert(NW * 4096 <= STAGE, "bf16 epilogue buffers must fit one stage");
     switch (p.epi) {
       case EPI_STORE:
-        epilogue_bf16<EPI_STORE, MB, NB, TAG == 1>(acc, p, buf16, row0, col0, lane);
+        if constexpr (NB == 2) epilogue_bf16<EPI_STORE, MB, NB, TAG == 1>(acc, p, buf16, row0, col0, lane);
+        else epilogue_rows<EPI_STORE, MB, NB>(acc, p, buf, row0, col0, lane);
         break;
       case EPI_BIAS_GELU:
-        epilogue_bf16<EPI_BIAS_GELU, MB, NB, false>(acc, p, buf16, row0, col0, lane);
+        if constexpr (NB == 2) epilogue_bf16<EPI_BIAS_GELU, MB, NB, false>(acc, p, buf16, row0, col0, lane);
+        else epilogue_rows<EPI_BIAS_GELU, MB, NB>(acc, p, buf, row0, col0, lane);
         break;
       case EPI_BIAS_RESID: epilogue_rows<EPI_BIAS_RESID, MB, NB>(acc, p, buf, row0, col0, lane); break;
       case EPI_GELU_BWD: epilogue_rows<EPI_GELU_BWD, MB, NB>(acc, p, buf, row0, col0, lane); break;
@@ -814,8 +818,8 @@ hipError_t launch_dma(int splits, int tag, const GemmParams& p, hipStream_t s) {
   constexpr int RB = 64;
   constexpr int STAGE = (BM + BN) * RB;
   constexpr int NSTAGE = 3;
-  constexpr int NW = BM == 256 ? 8 : 4;
-  constexpr int MINB = BM == 256 ? 1 : 2;
+  constexpr int NW = BM + BN >= 512 ? 8 : 4;
+  constexpr int MINB = NW == 8 ? 1 : 2;
   static_assert(NSTAGE * STAGE * MINB <= 160 * 1024, "LDS");
   const int tiles = ((p.M + BM - 1) / BM) * ((p.N + BN - 1) / BN);
   if constexpr (AK == 1 && BKM == 1 && BM == 256) {
@@ -864,6 +868,14 @@ hipError_t launch_type(int a_kmajor, int b_kmajor, int tile, int splits, int tag
     return launch_layout<T, 128, 128>(a_kmajor, b_kmajor, splits, tag, p, s);
   } else {
     switch (tile) {
+      case TILE_128x384:
+        // k-major A only (its loads all go out in the first k-step), and not with the column sums
+        // of the GELU-backward epilogue
+        if (a_kmajor && !p.colsum) {
+          if (b_kmajor) return launch_t<T, 1, 1, 128, 384>(splits, tag, p, s);
+          return launch_t<T, 1, 0, 128, 384>(splits, tag, p, s);
+        }
+        return launch_layout<T, 256, 256>(a_kmajor, b_kmajor, splits, tag, p, s);
       case TILE_256: return launch_layout<T, 256, 256>(a_kmajor, b_kmajor, splits, tag, p, s);
       default: return launch_layout<T, 128, 128>(a_kmajor, b_kmajor, splits, tag, p, s);
     }
@@ -876,6 +888,9 @@ int gemm_k_tile(bool is_bf16) { return is_bf16 ? ROWB / 2 : ROWB / 4; }
 
 int gemm_pick_tile(int M, int N) {
   const int64_t t256 = (int64_t)((M + 255) / 256) * ((N + 255) / 256);
+  // An output of 192 .. 255 tiles of 256 x 256 leaves CUs idle for the whole product; where N is
+  // a multiple of 384 the 128 x 384 tile (same block shape, 8 waves) splits it into 4/3 as many.
+  if (t256 >= 192 && t256 < 256 && N % 384 == 0) return TILE_128x384;
   return t256 >= 192 ? TILE_256 : TILE_128;
 }
 

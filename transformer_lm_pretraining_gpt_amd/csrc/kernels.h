@@ -34,7 +34,7 @@ struct GemmParams {
   float* colsum;
 };
 
-enum GemmTile { TILE_128 = 0, TILE_256 = 1 };
+enum GemmTile { TILE_128 = 0, TILE_256 = 1, TILE_128x384 = 2 };
 
 // Launch C = op(A) op(B) with the given operand layouts (1 = k contiguous). is_bf16 selects the
 // element type of A, B, C(T), C2, aux. splits > 1 requires epi == EPI_F32.

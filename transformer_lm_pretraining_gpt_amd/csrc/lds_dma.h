@@ -80,7 +80,8 @@ DEV void wait_slabs_lgkm0(int after) {
 // XOR with 4. Either way the result stays inside the k-row.
 template <int R>
 DEV int tr_swz(int krow) {
-  static_assert(R >= 64 && R % 64 == 0, "transposed tiles are at least 64 columns wide");
+  // R a multiple of 128 past 128: the XOR (< 16) stays inside the k-row's 16-chunk groups
+  static_assert(R == 64 || R % 128 == 0, "transposed tiles of 64 or a multiple of 128 columns");
   if constexpr (R == 64) return ((krow >> 1) & 1) << 2;
   else return (krow & 3) << 2;
 }
@@ -115,10 +116,12 @@ struct DmaTile {
         const int r = min(r0 + row, r_total - 1);
         off[i] = (uint32_t)((int64_t)(r - r0) * ld * 2 + c * 16);
       } else {
+        // the slab's k-rows are laid out one after another, 64 chunks per wave-load (a wave-load
+        // may end inside a k-row when 2R does not divide 1 KB)
         constexpr int CPR = R / 8;            // 16-byte chunks per k-row
-        constexpr int KPI = 1024 / (2 * R);   // k-rows per wave-load
-        const int krow = q * KPI + lane / CPR;
-        const int c = (lane % CPR) ^ tr_swz<R>(krow);
+        const int pos = q * 64 + lane;
+        const int krow = pos / CPR;
+        const int c = (pos % CPR) ^ tr_swz<R>(krow);
         int r = r0 + c * 8;
         if (r >= r_total) r = r_total - 8;  // r_total and r0 are multiples of 8: r >= r0
         off[i] = (uint32_t)((int64_t)krow * ld * 2 + (r - r0) * 2);

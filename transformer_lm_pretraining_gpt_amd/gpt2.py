@@ -83,6 +83,9 @@ def load_library(path: str | None = None):
         "gpt2_op_gemm": (st, [c_int32, c_int32, c_int32, c_int32, c_int32, c_int32, c_void_p,
                               c_int64, c_void_p, c_int64, c_void_p, c_int64, c_float, c_float,
                               c_void_p]),
+        "gpt2_op_gemm_epilogue": (st, [c_int32, c_int32, c_int32, c_int32, c_int32, c_void_p,
+                                       c_int64, c_void_p, c_int64, c_int32, c_void_p, c_void_p,
+                                       c_int64, c_void_p, c_void_p, c_float, c_void_p]),
         "gpt2_op_attention_forward": (st, [c_int32, c_int32, c_int32, c_int32, c_int32, c_void_p,
                                            c_void_p, c_void_p, c_void_p]),
         "gpt2_op_attention_backward": (st, [c_int32, c_int32, c_int32, c_int32, c_int32, c_void_p,
@@ -225,6 +228,19 @@ def op_gemm(a, b, c, *, a_kmajor: bool, b_kmajor: bool, m: int, n: int, k: int, 
     _check(lib.gpt2_op_gemm(prec, int(a_kmajor), int(b_kmajor), m, n, k, a.data_ptr(), lda,
                             b.data_ptr(), ldb, c.data_ptr(), c.shape[-1], alpha, beta,
                             torch.cuda.current_stream().cuda_stream))
+
+
+EPI_STORE, EPI_BIAS_GELU, EPI_BIAS_RESID, EPI_GELU_BWD = 0, 1, 2, 3
+
+
+def op_gemm_epilogue(a, b, c, *, a_kmajor: bool, b_kmajor: bool, m: int, n: int, k: int,
+                     epilogue: int, c2=None, bias=None, aux=None, alpha=1.0):
+    import torch
+    lib = load_library()
+    _check(lib.gpt2_op_gemm_epilogue(int(a_kmajor), int(b_kmajor), m, n, k, a.data_ptr(),
+                                     a.shape[-1], b.data_ptr(), b.shape[-1], epilogue,
+                                     c.data_ptr(), _ptr(c2), c.shape[-1], _ptr(bias), _ptr(aux),
+                                     alpha, torch.cuda.current_stream().cuda_stream))
 
 
 def op_attention_forward(qkv, out, lse, batch, seq_len, n_head, head_dim, precision="bf16"):
