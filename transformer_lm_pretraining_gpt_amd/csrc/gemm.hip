@@ -42,6 +42,25 @@ DEV float gelu_tanh_grad(float u) {
   return 0.5f * (1.0f + t) + 0.5f * u * (1.0f - t * t) * c * (1.0f + 3.0f * a * u * u);
 }
 
+// The same two functions for the bf16 direct-to-LDS epilogues, where they run on every element
+// of a product with no MFMA work to hide them: with z = c (u + a u^3), (1 + tanh z) / 2 = s =
+// 1 / (1 + e^(-2z)), so gelu(u) = u s and gelu'(u) = s + 2 u s (1 - s) c (1 + 3 a u^2); one
+// v_exp_f32 and one v_rcp_f32 per element instead of tanhf (measured: the bias + GELU product
+// 28 % faster, the GELU-backward one 16 %). Large |u| saturate to s = 0 or 1 (exp2 overflowing
+// to +inf gives rcp = 0). Error: a few fp32 ulps of s (absolute ~1e-7 in s (1 - s)).
+constexpr float GELU_E1 = -2.0f * 0.7978845608028654f * 1.4426950408889634f;  // -2c log2(e)
+constexpr float GELU_E3 = GELU_E1 * 0.044715f;
+DEV float gelu_sigmoid(float u, float u2) {  // s = 1 / (1 + 2^(-2z log2 e))
+  return __builtin_amdgcn_rcpf(1.0f + fast_exp2(u * fmaf(GELU_E3, u2, GELU_E1)));
+}
+DEV float gelu_fast(float u) { return u * gelu_sigmoid(u, u * u); }
+DEV float gelu_grad_fast(float u) {
+  const float u2 = u * u;
+  const float s = gelu_sigmoid(u, u2);
+  constexpr float c2 = 2.0f * 0.7978845608028654f, c6 = c2 * 3.0f * 0.044715f;
+  return fmaf(u * (s - s * s), fmaf(c6, u2, c2), s);
+}
+
 // Global -> register -> LDS movement of one operand tile of R rows x one k-slab.
 // KMAJOR: stored [r][k] (ld = row pitch in elements); else stored [k][r].
 template <typename T, int R, bool KMAJOR>
@@ -318,8 +337,8 @@ DEV void epilogue_bf16(const f32x16 (&acc)[MB][NB], const GemmParams& p, char* b
             x0 = acc[i][j][r] + bias[j];
             x1 = acc[i][j][r + 1] + bias[j];
             if (out == 1) {
-              x0 = gelu_tanh(x0);
-              x1 = gelu_tanh(x1);
+              x0 = gelu_fast(x0);
+              x1 = gelu_fast(x1);
             }
           }
           const uint32_t pk = pack_bf16(x0, x1);
@@ -391,7 +410,7 @@ DEV void epilogue_rows(const f32x16 (&acc)[MB][NB], const GemmParams& p, float* 
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
               out[e] = v[e] + bias[e];
-              gl[e] = gelu_tanh(out[e]);
+              gl[e] = gelu_fast(out[e]);
             }
             st8(static_cast<bf16*>(p.C) + o, u32x2{pack_bf16(out[0], out[1]), pack_bf16(out[2], out[3])});
             st8(static_cast<bf16*>(p.C2) + o, u32x2{pack_bf16(gl[0], gl[1]), pack_bf16(gl[2], gl[3])});
@@ -403,7 +422,7 @@ DEV void epilogue_rows(const f32x16 (&acc)[MB][NB], const GemmParams& p, float* 
             const float uf[4] = {bf16lo(u[0]), bf16hi(u[0]), bf16lo(u[1]), bf16hi(u[1])};
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
-              out[e] = v[e] * gelu_tanh_grad(uf[e]);
+              out[e] = v[e] * gelu_grad_fast(uf[e]);
               csum[e] += out[e];
             }
             st8(static_cast<bf16*>(p.C) + o, u32x2{pack_bf16(out[0], out[1]), pack_bf16(out[2], out[3])});
