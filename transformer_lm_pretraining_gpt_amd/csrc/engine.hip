@@ -175,6 +175,33 @@ Split pick_split(const Geo& g, int in, int out) {
   return {s, per};
 }
 
+// Column sums of the backward (bias, LayerNorm gain and shift gradients): every reduction writes
+// its partial rows to a slice of its own and all are summed by one batched launch at the end
+// of the backward (49 launches of a few microseconds each before). Slices: LayerNorm k = 2l
+// (ln1 of layer l), 2l + 1 (ln2), 2L (final); then the QKV bias per layer; then the fc bias.
+struct ColLayout {
+  size_t ln, qkv, fc, total;  // floats per slice, and in all
+  int nparts_ln, nparts_qkv, nparts_fc, ntasks;
+};
+ColLayout col_layout(const Geo& g) {
+  ColLayout cl{};
+  const size_t d = g.d;
+  cl.nparts_ln = ln_bwd_blocks(g.M, LN_ROWS_PER_BLOCK);
+  cl.nparts_qkv = (g.M + COLSUM_ROWS_PER_BLOCK - 1) / COLSUM_ROWS_PER_BLOCK;
+  if (fused_colsum(g)) {
+    const int bm = pick_tile(g, g.M, 4 * g.d) == TILE_256 ? 256 : 128;
+    cl.nparts_fc = 2 * ((g.M + bm - 1) / bm);
+  } else {
+    cl.nparts_fc = cl.nparts_qkv;
+  }
+  cl.ln = (size_t)cl.nparts_ln * 3 * d;
+  cl.qkv = (size_t)cl.nparts_qkv * 3 * d;
+  cl.fc = (size_t)cl.nparts_fc * 4 * d;
+  cl.total = (2 * (size_t)g.L + 1) * cl.ln + (size_t)g.L * (cl.qkv + cl.fc);
+  cl.ntasks = 4 * g.L + 1;
+  return cl;
+}
+
 // ------------------------------------------------------------------------------ buffers
 struct Bufs {
   float *params = nullptr, *grads = nullptr, *m = nullptr, *v = nullptr;
@@ -192,7 +219,9 @@ struct Bufs {
   float* dtmp = nullptr;
   void *dbig = nullptr, *dqkv = nullptr, *datt = nullptr;
   float* dsum = nullptr;
-  float* colpart = nullptr;
+  float* colpart = nullptr;      // column-sum partial rows: one slice per reduction of a backward
+  ColTask* coltasks = nullptr;   // the reductions of those slices (device table, built at init)
+  int ncoltasks = 0, ncolblocks = 0;
   float* splitk = nullptr;
   uint32_t* keys = nullptr;
   float* segpart = nullptr;
@@ -258,7 +287,11 @@ size_t carve(const Geo& g, uintptr_t base, Bufs& b) {
   b.dsum = c.take<float>(8 * bht);  // attention backward scratch: 2 floats per (b, h, t)
   const size_t nblk = (size_t)ln_bwd_blocks(g.M, LN_ROWS_PER_BLOCK);
   const size_t ncs = (M + COLSUM_ROWS_PER_BLOCK - 1) / COLSUM_ROWS_PER_BLOCK;
-  b.colpart = c.take<float>(4 * std::max(nblk * 3 * d, ncs * 4 * d));
+  (void)nblk;
+  (void)ncs;
+  const ColLayout cl = col_layout(g);
+  b.colpart = c.take<float>(4 * cl.total);
+  b.coltasks = c.take<ColTask>(sizeof(ColTask) * cl.ntasks);
   size_t sk = 0;
   const int shapes[4][2] = {{g.d, 3 * g.d}, {g.d, g.d}, {g.d, 4 * g.d}, {4 * g.d, g.d}};
   for (auto& s : shapes) {
@@ -274,6 +307,45 @@ size_t carve(const Geo& g, uintptr_t base, Bufs& b) {
 }  // namespace
 
 // ------------------------------------------------------------------------------ context
+namespace {
+float* ln_part(const Geo& g, const Bufs& b, int k) { return b.colpart + (size_t)k * col_layout(g).ln; }
+float* qkv_part(const Geo& g, const Bufs& b, int l) {
+  const ColLayout cl = col_layout(g);
+  return b.colpart + (2 * (size_t)g.L + 1) * cl.ln + (size_t)l * cl.qkv;
+}
+float* fc_part(const Geo& g, const Bufs& b, int l) {
+  const ColLayout cl = col_layout(g);
+  return b.colpart + (2 * (size_t)g.L + 1) * cl.ln + (size_t)g.L * cl.qkv + (size_t)l * cl.fc;
+}
+
+// The backward's column reductions over those slices (in any order: their outputs are disjoint)
+std::vector<ColTask> col_tasks(const Geo& g, const Bufs& b) {
+  const ColLayout cl = col_layout(g);
+  float* G = b.grads;
+  const int d = g.d;
+  std::vector<ColTask> t;
+  auto add = [&](const float* part, int nparts, int64_t stride, int seg, float* o0, float* o1,
+                 float* o2) {
+    const int nseg = o2 ? 3 : (o1 ? 2 : 1);
+    t.push_back(ColTask{part, stride, nparts, nseg * seg, seg, 0, {o0, o1, o2}});
+  };
+  add(ln_part(g, b, 2 * g.L), cl.nparts_ln, 3 * d, d, G + g.lnfg, G + g.lnfb, G + g.bproj(g.L - 1));
+  for (int l = g.L - 1; l >= 0; --l) {
+    add(fc_part(g, b, l), cl.nparts_fc, 4 * d, 4 * d, G + g.bfc(l), nullptr, nullptr);
+    add(ln_part(g, b, 2 * l + 1), cl.nparts_ln, 3 * d, d, G + g.ln2g(l), G + g.ln2b(l), G + g.bo(l));
+    add(qkv_part(g, b, l), cl.nparts_qkv, 3 * d, 3 * d, G + g.bqkv(l), nullptr, nullptr);
+    add(ln_part(g, b, 2 * l), cl.nparts_ln, 3 * d, d, G + g.ln1g(l), G + g.ln1b(l),
+        l > 0 ? G + g.bproj(l - 1) : nullptr);
+  }
+  int blk = 0;
+  for (ColTask& k : t) {
+    k.block0 = blk;
+    blk += (k.n + 63) / 64;
+  }
+  return t;
+}
+}  // namespace
+
 struct gpt2_ctx {
   gpt2_config cfg;
   Geo g;
@@ -359,27 +431,21 @@ gpt2_status gemm_dw(gpt2_ctx* c, int in, int out, const void* X, const void* dY,
   return GPT2_OK;
 }
 
-gpt2_status colsum(gpt2_ctx* c, const void* src, int N, float* out, int accumulate) {
+// Column partial sums of an (M, N) matrix into `part` (reduced with the others at the end)
+gpt2_status colsum(gpt2_ctx* c, const void* src, int N, float* part) {
   const Geo& g = c->g;
-  const int nparts = (g.M + COLSUM_ROWS_PER_BLOCK - 1) / COLSUM_ROWS_PER_BLOCK;
-  HIPCHK(launch_colsum_partial(g.bf16, g.M, N, src, N, c->b.colpart, COLSUM_ROWS_PER_BLOCK,
-                               c->stream));
-  HIPCHK(launch_colsum_reduce(c->b.colpart, nparts, N, N, out, accumulate, c->stream));
+  HIPCHK(launch_colsum_partial(g.bf16, g.M, N, src, N, part, COLSUM_ROWS_PER_BLOCK, c->stream));
   return GPT2_OK;
 }
 
-// LayerNorm backward into the residual gradient, then its three column sums: gain and shift
-// gradients, and (when bias_out is not NULL) the bias gradient of the projection that produced
-// this residual stream.
+// LayerNorm backward into the residual gradient; its three column partial sums (gain and shift
+// gradients, and the bias gradient of the projection that produced this residual stream) go to
+// LayerNorm slice k and are reduced with the others at the end of the backward.
 gpt2_status ln_backward(gpt2_ctx* c, const float* x, const float* mean, const float* rstd,
-                        int64_t g_off, int64_t b_off, float* bias_out, int has_dres,
-                        int accumulate) {
+                        int64_t g_off, int has_dres, int k) {
   const Geo& g = c->g;
-  const int nblk = ln_bwd_blocks(g.M, LN_ROWS_PER_BLOCK);
   HIPCHK(launch_ln_bwd(g.bf16, g.M, g.d, c->b.dtmp, x, mean, rstd, c->b.params + g_off, c->b.dres,
-                       has_dres, c->b.dres_t, c->b.colpart, LN_ROWS_PER_BLOCK, c->stream));
-  HIPCHK(launch_colsum_reduce3(c->b.colpart, nblk, 3 * (int64_t)g.d, g.d, c->b.grads + g_off,
-                               c->b.grads + b_off, bias_out, accumulate, c->stream));
+                       has_dres, c->b.dres_t, ln_part(g, c->b, k), LN_ROWS_PER_BLOCK, c->stream));
   return GPT2_OK;
 }
 
@@ -446,8 +512,7 @@ gpt2_status backward(gpt2_ctx* c, float grad_scale, int acc) {
     Timed t(c, FAM_GEMM, 2.0 * g.Vp * d * M);
     HIPCHK(launch_gemm(g.bf16, 0, 0, pick_tile(g, g.Vp, d), 1, 0, p, c->stream));
   }
-  STEP(ln_backward(c, b.resid[g.L], b.lnf_mean, b.lnf_rstd, g.lnfg, g.lnfb, G + g.bproj(g.L - 1),
-                   0, acc));
+  STEP(ln_backward(c, b.resid[g.L], b.lnf_mean, b.lnf_rstd, g.lnfg, 0, 2 * g.L));
   for (int l = g.L - 1; l >= 0; --l) {
     // h_{l+1} = h_mid + act W_proj + b_proj ; dres holds dh_{l+1}
     STEP(gemm_dw(c, 4 * d, d, b.act[l], b.dres_t, G + g.wproj(l), acc));
@@ -455,33 +520,30 @@ gpt2_status backward(gpt2_ctx* c, float grad_scale, int acc) {
     // product's epilogue as one partial row per 128 (or 64) rows when it runs the direct-to-LDS
     // bf16 path, else from a separate pass
     if (fused_colsum(g)) {
-      const int bm = pick_tile(g, M, 4 * d) == TILE_256 ? 256 : 128;
       STEP(gemm(c, 1, 1, M, 4 * d, d, b.dres_t, d, W(c, g.wproj(l)), d, EPI_GELU_BWD, b.dbig,
-                4 * d, nullptr, nullptr, nullptr, b.fc[l], 1.0f, 0.0f, 0, b.colpart));
-      HIPCHK(launch_colsum_reduce(b.colpart, 2 * ((M + bm - 1) / bm), 4 * d, 4 * d, G + g.bfc(l),
-                                  acc, c->stream));
+                4 * d, nullptr, nullptr, nullptr, b.fc[l], 1.0f, 0.0f, 0, fc_part(g, b, l)));
     } else {
       STEP(gemm(c, 1, 1, M, 4 * d, d, b.dres_t, d, W(c, g.wproj(l)), d, EPI_GELU_BWD, b.dbig,
                 4 * d, nullptr, nullptr, nullptr, b.fc[l]));
-      STEP(colsum(c, b.dbig, 4 * d, G + g.bfc(l), acc));
+      STEP(colsum(c, b.dbig, 4 * d, fc_part(g, b, l)));
     }
     STEP(gemm_dw(c, d, 4 * d, b.ln2[l], b.dbig, G + g.wfc(l), acc));
     STEP(gemm(c, 1, 1, M, d, 4 * d, b.dbig, 4 * d, W(c, g.wfc(l)), 4 * d, EPI_F32, b.dtmp, d));
-    STEP(ln_backward(c, b.resid_mid[l], b.ln2_mean[l], b.ln2_rstd[l], g.ln2g(l), g.ln2b(l),
-                     G + g.bo(l), 1, acc));
+    STEP(ln_backward(c, b.resid_mid[l], b.ln2_mean[l], b.ln2_rstd[l], g.ln2g(l), 1, 2 * l + 1));
     // h_mid = h_l + att W_o + b_o ; dres holds dh_mid
     STEP(gemm_dw(c, d, d, b.att[l], b.dres_t, G + g.wo(l), acc));
     STEP(gemm(c, 1, 1, M, d, d, b.dres_t, d, W(c, g.wo(l)), d, EPI_STORE, b.datt, d));
     HIPCHK(launch_attn_bwd(g.bf16, g.B, g.T, g.H, g.hd, b.qkv[l], b.att[l], b.lse[l], b.datt,
                            b.dqkv, b.dsum, c->stream));
-    STEP(colsum(c, b.dqkv, 3 * d, G + g.bqkv(l), acc));
+    STEP(colsum(c, b.dqkv, 3 * d, qkv_part(g, b, l)));
     STEP(gemm_dw(c, d, 3 * d, b.ln1[l], b.dqkv, G + g.wqkv(l), acc));
     STEP(gemm(c, 1, 1, M, d, 3 * d, b.dqkv, 3 * d, W(c, g.wqkv(l)), 3 * d, EPI_F32, b.dtmp, d));
-    STEP(ln_backward(c, b.resid[l], b.ln1_mean[l], b.ln1_rstd[l], g.ln1g(l), g.ln1b(l),
-                     l > 0 ? G + g.bproj(l - 1) : nullptr, 1, acc));
+    STEP(ln_backward(c, b.resid[l], b.ln1_mean[l], b.ln1_rstd[l], g.ln1g(l), 1, 2 * l));
   }
   HIPCHK(launch_embed_bwd(g.B, g.T, d, b.keys, b.dres, G + g.wte, G + g.wpe, acc, b.segpart,
                           c->stream));
+  // every bias and LayerNorm gain/shift gradient from its partial rows, in one launch
+  HIPCHK(launch_colsum_reduce_batch(b.coltasks, b.ncoltasks, b.ncolblocks, acc, c->stream));
   return GPT2_OK;
 }
 
@@ -556,6 +618,11 @@ gpt2_status gpt2_init(const gpt2_config* cfg, void* d_arena, size_t arena_bytes,
   INITCHK(hipMemsetAsync(b.err, 0, sizeof(int), c->stream));
   INITCHK(hipMemsetAsync(b.loss, 0, sizeof(float), c->stream));
   INITCHK(hipMemcpyAsync(b.segs, c->segs.data(), sizeof(AdamSeg) * c->segs.size(),
+                         hipMemcpyHostToDevice, c->stream));
+  const std::vector<ColTask> coltasks = col_tasks(g, b);
+  b.ncoltasks = (int)coltasks.size();
+  b.ncolblocks = coltasks.empty() ? 0 : coltasks.back().block0 + (coltasks.back().n + 63) / 64;
+  INITCHK(hipMemcpyAsync(b.coltasks, coltasks.data(), sizeof(ColTask) * coltasks.size(),
                          hipMemcpyHostToDevice, c->stream));
   INITCHK(hipStreamSynchronize(c->stream));
 #undef INITCHK

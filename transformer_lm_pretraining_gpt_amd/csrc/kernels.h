@@ -71,6 +71,19 @@ int ln_bwd_blocks(int M, int rows_per_block);
 // Column partial sums of a (M, N) matrix (T or fp32) per block of rows: part[blk][N].
 hipError_t launch_colsum_partial(bool src_bf16, int M, int N, const void* src, int64_t ld,
                                  float* part, int rows_per_block, hipStream_t s);
+// One column reduction of a batch: columns [0, n) of the partial rows part[p * stride + j],
+// p < nparts, column j going to out[j / seg][j % seg] (a NULL output drops its columns). block0
+// is the task's first block in the batched launch (64 columns per block, tasks in order).
+struct ColTask {
+  const float* part;
+  int64_t stride;
+  int nparts, n, seg, block0;
+  float* out[3];
+};
+// Every task of d_tasks (device memory) in one launch of nblocks blocks, each column summed in
+// the same fixed order as launch_colsum_reduce3.
+hipError_t launch_colsum_reduce_batch(const ColTask* d_tasks, int ntasks, int nblocks,
+                                      int accumulate, hipStream_t s);
 // out[j] = (accumulate ? out[j] : 0) + sum_p part[p * stride + j], fixed p order, j < n.
 hipError_t launch_colsum_reduce(const float* part, int nparts, int64_t stride, int n, float* out,
                                 int accumulate, hipStream_t s);

@@ -192,12 +192,11 @@ struct ColOut {
 };
 constexpr int RED_WAVES = 16;
 
-__global__ __launch_bounds__(64 * RED_WAVES) void colsum_reduce_kernel(
-    const float* __restrict__ part, int nparts, int64_t stride, int n, int seg, ColOut outs,
-    int accumulate) {
+DEV void colsum_reduce_block(const float* __restrict__ part, int nparts, int64_t stride, int n,
+                             int seg, float* const (&outs)[3], int accumulate, int chunk) {
   __shared__ float sh[RED_WAVES][64];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int j = blockIdx.x * 64 + lane;
+  const int j = chunk * 64 + lane;
   float a0 = 0.0f, a1 = 0.0f, a2 = 0.0f, a3 = 0.0f;
   if (j < n) {
     int p = wave;
@@ -214,12 +213,29 @@ __global__ __launch_bounds__(64 * RED_WAVES) void colsum_reduce_kernel(
   if (wave == 0 && j < n) {
     float s = 0.0f;
     for (int w = 0; w < RED_WAVES; ++w) s += sh[w][lane];
-    float* o = outs.out[j / seg];
+    float* o = outs[j / seg];
     if (o) {
       const int c = j % seg;
       o[c] = accumulate ? o[c] + s : s;
     }
   }
+}
+
+__global__ __launch_bounds__(64 * RED_WAVES) void colsum_reduce_kernel(
+    const float* __restrict__ part, int nparts, int64_t stride, int n, int seg, ColOut outs,
+    int accumulate) {
+  colsum_reduce_block(part, nparts, stride, n, seg, outs.out, accumulate, blockIdx.x);
+}
+
+// The batch: block b finds the last task whose first block is <= b (tasks are few).
+__global__ __launch_bounds__(64 * RED_WAVES) void colsum_reduce_batch_kernel(
+    const ColTask* __restrict__ tasks, int ntasks, int accumulate) {
+  const int blk = blockIdx.x;
+  int t = 0;
+  while (t + 1 < ntasks && tasks[t + 1].block0 <= blk) ++t;
+  const ColTask& tk = tasks[t];
+  float* const outs[3] = {tk.out[0], tk.out[1], tk.out[2]};
+  colsum_reduce_block(tk.part, tk.nparts, tk.stride, tk.n, tk.seg, outs, accumulate, blk - tk.block0);
 }
 
 }  // namespace
@@ -292,6 +308,14 @@ hipError_t launch_colsum_partial(bool src_bf16, int M, int N, const void* src, i
   else
     hipLaunchKernelGGL(colsum_partial_kernel<float>, grid, dim3(256), 0, s, M, N,
                        static_cast<const float*>(src), ld, part, rows_per_block);
+  return hipGetLastError();
+}
+
+hipError_t launch_colsum_reduce_batch(const ColTask* d_tasks, int ntasks, int nblocks,
+                                      int accumulate, hipStream_t s) {
+  if (ntasks == 0 || nblocks == 0) return hipSuccess;
+  hipLaunchKernelGGL(colsum_reduce_batch_kernel, dim3(nblocks), dim3(64 * RED_WAVES), 0, s, d_tasks,
+                     ntasks, accumulate);
   return hipGetLastError();
 }
 
