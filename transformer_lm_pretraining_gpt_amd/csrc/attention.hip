@@ -735,17 +735,18 @@ __global__ __launch_bounds__(THREADS, 2) void attn_bwd_dkdv64_kernel(
     const char* dot = qt + 8192;
     const float* ls = reinterpret_cast<const float*>(qt + 16384);
     const int q = (qt0 + t) * 64;
-#pragma unroll
-    for (int ib = 0; ib < 2; ++ib) {
-      const int iq = q + ib * 32;
-      if (iq + 31 < kg) continue;  // every query of the sub-tile is before this wave's keys
-      const bool diag = iq < kg + 32;
-      f32x16 sacc = f32x16{}, dpacc = f32x16{};
+    // one 32-query sub-tile in three steps: S and dP, then P and dS, then dV and dK
+    auto scores = [&](int ib, f32x16& sacc, f32x16& dpacc) {
+      sacc = f32x16{};
+      dpacc = f32x16{};
 #pragma unroll
       for (int s = 0; s < 4; ++s) {
         Mfma<bf16>::mma(sacc, HeadTile::frag(qt, ib * 32, s, lane), kf[s]);
         Mfma<bf16>::mma(dpacc, HeadTile::frag(dot, ib * 32, s, lane), vf[s]);
       }
+    };
+    auto probs = [&](int ib, bool diag, const f32x16& sacc, const f32x16& dpacc, u32x4 (&pb)[2],
+                     u32x4 (&dsb)[2]) {
       float p[16], ds[16];
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
@@ -764,12 +765,41 @@ __global__ __launch_bounds__(THREADS, 2) void attn_bwd_dkdv64_kernel(
       }
 #pragma unroll
       for (int u = 0; u < 2; ++u) {
-        const u32x4 pb = pack8(p + 8 * u), dsb = pack8(ds + 8 * u);
+        pb[u] = pack8(p + 8 * u);
+        dsb[u] = pack8(ds + 8 * u);
+      }
+    };
+    auto accumulate = [&](int ib, const u32x4 (&pb)[2], const u32x4 (&dsb)[2]) {
+#pragma unroll
+      for (int u = 0; u < 2; ++u)
 #pragma unroll
         for (int db = 0; db < 2; ++db) {
-          Mfma<bf16>::mma(dv[db], HeadTile::tfrag(dot, db * 32, ib * 32 + 16 * u, lane), pb);
-          Mfma<bf16>::mma(dk[db], HeadTile::tfrag(qt, db * 32, ib * 32 + 16 * u, lane), dsb);
+          Mfma<bf16>::mma(dv[db], HeadTile::tfrag(dot, db * 32, ib * 32 + 16 * u, lane), pb[u]);
+          Mfma<bf16>::mma(dk[db], HeadTile::tfrag(qt, db * 32, ib * 32 + 16 * u, lane), dsb[u]);
         }
+    };
+    if (q >= kg + 32) {
+      // every query of the tile is after this wave's keys (no mask): both sub-tiles as one
+      // straight-line block, so that one's MFMAs can overlap the other's exponentials
+      f32x16 s0, d0, s1, d1;
+      u32x4 pb0[2], ds0[2], pb1[2], ds1[2];
+      scores(0, s0, d0);
+      scores(1, s1, d1);
+      probs(0, false, s0, d0, pb0, ds0);
+      accumulate(0, pb0, ds0);
+      probs(1, false, s1, d1, pb1, ds1);
+      accumulate(1, pb1, ds1);
+    } else {
+#pragma unroll
+      for (int ib = 0; ib < 2; ++ib) {
+        const int iq = q + ib * 32;
+        if (iq + 31 < kg) continue;  // every query of the sub-tile is before this wave's keys
+        const bool diag = iq < kg + 32;
+        f32x16 sacc, dpacc;
+        u32x4 pb[2], dsb[2];
+        scores(ib, sacc, dpacc);
+        probs(ib, diag, sacc, dpacc, pb, dsb);
+        accumulate(ib, pb, dsb);
       }
     }
     };
