@@ -757,11 +757,14 @@ __global__ __launch_bounds__(THREADS, 2) void attn_bwd_dkdv64_kernel(
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           const int r = 4 * g + e;
-          float pr = fast_exp2(fmaf(sacc[r], c, -lv[e]));
-          if (diag && q + il + e < kj) pr = 0.0f;
-          p[r] = pr;
-          ds[r] = pr * (dpacc[r] - dd[e]);
+          p[r] = fast_exp2(fmaf(sacc[r], c, -lv[e]));
+          ds[r] = p[r] * (dpacc[r] - dd[e]);
         }
+      }
+      if (diag) {  // queries before the key: zero (a branch of its own, taken on diagonal tiles)
+#pragma unroll
+        for (int r = 0; r < 16; ++r)
+          if (q + ib * 32 + mfma_row(r, h) < kj) p[r] = ds[r] = 0.0f;
       }
 #pragma unroll
       for (int u = 0; u < 2; ++u) {
@@ -879,30 +882,59 @@ __global__ __launch_bounds__(THREADS, 2) void attn_bwd_dq64_kernel(
     for (int i = 0; i < 2; ++i) {
       if (key0 > qg[i] + 31 || qg[i] >= T_) continue;  // every key of the tile is after the group
       const int qi = qg[i] + l32;
-#pragma unroll
-      for (int js = 0; js < 2; ++js) {
-        const int j0 = key0 + js * 32;
-        if (j0 > qg[i] + 31) continue;
-        const bool diag = j0 + 31 > qg[i];
-        f32x16 sacc = f32x16{}, dpacc = f32x16{};
+      // one 32-key sub-tile in three steps: S^T and dP^T, then dS^T, then dQ^T
+      auto scores = [&](int js, f32x16& sacc, f32x16& dpacc) {
+        sacc = f32x16{};
+        dpacc = f32x16{};
 #pragma unroll
         for (int s = 0; s < 4; ++s) {
           Mfma<bf16>::mma(sacc, HeadTile::frag(ktile, js * 32, s, lane), qf[i][s]);
           Mfma<bf16>::mma(dpacc, HeadTile::frag(vtile, js * 32, s, lane), df[i][s]);
         }
+      };
+      auto dscores = [&](int js, bool diag, const f32x16& sacc, const f32x16& dpacc,
+                         u32x4 (&dsb)[2]) {
         float ds[16];
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          float pr = fast_exp2(fmaf(sacc[r], c, -lse2[i]));
-          if (diag && j0 + mfma_row(r, h) > qi) pr = 0.0f;
-          ds[r] = pr * (dpacc[r] - dsum[i]);
+        for (int r = 0; r < 16; ++r)
+          ds[r] = fast_exp2(fmaf(sacc[r], c, -lse2[i])) * (dpacc[r] - dsum[i]);
+        if (diag) {  // keys after the query: zero (a branch of its own, taken on diagonal tiles)
+          const int j0 = key0 + js * 32;
+#pragma unroll
+          for (int r = 0; r < 16; ++r)
+            if (j0 + mfma_row(r, h) > qi) ds[r] = 0.0f;
         }
 #pragma unroll
-        for (int u = 0; u < 2; ++u) {
-          const u32x4 dsb = pack8(ds + 8 * u);
+        for (int u = 0; u < 2; ++u) dsb[u] = pack8(ds + 8 * u);
+      };
+      auto accumulate = [&](int js, const u32x4 (&dsb)[2]) {
+#pragma unroll
+        for (int u = 0; u < 2; ++u)
 #pragma unroll
           for (int db = 0; db < 2; ++db)
-            Mfma<bf16>::mma(dq[i][db], HeadTile::tfrag(ktile, db * 32, js * 32 + 16 * u, lane), dsb);
+            Mfma<bf16>::mma(dq[i][db], HeadTile::tfrag(ktile, db * 32, js * 32 + 16 * u, lane), dsb[u]);
+      };
+      if (key0 + 63 <= qg[i]) {
+        // every key of the tile is at or before every query of the group (no mask): both
+        // sub-tiles as one straight-line block
+        f32x16 s0, d0, s1, d1;
+        u32x4 ds0[2], ds1[2];
+        scores(0, s0, d0);
+        scores(1, s1, d1);
+        dscores(0, false, s0, d0, ds0);
+        accumulate(0, ds0);
+        dscores(1, false, s1, d1, ds1);
+        accumulate(1, ds1);
+      } else {
+#pragma unroll
+        for (int js = 0; js < 2; ++js) {
+          const int j0 = key0 + js * 32;
+          if (j0 > qg[i] + 31) continue;
+          f32x16 sacc, dpacc;
+          u32x4 dsb[2];
+          scores(js, sacc, dpacc);
+          dscores(js, j0 + 31 > qg[i], sacc, dpacc, dsb);
+          accumulate(js, dsb);
         }
       }
     }
