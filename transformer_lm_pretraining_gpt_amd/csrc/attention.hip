@@ -353,18 +353,18 @@ __global__ __launch_bounds__(THREADS, 3) void attn_fwd64_kernel(const bf16* __re
     const char* ktile = smem + ST * F64_STAGE;
     const char* vtile = ktile + 8192;
     const int key0 = kt * 64;
-#pragma unroll
-    for (int i = 0; i < 2; ++i) {
-      if (key0 > qg[i] + 31 || qg[i] >= T_) continue;  // every key of the tile is after the group
-      const bool diag = key0 + 63 > qg[i];
-      const int qi = qg[i] + l32;
-      f32x16 sacc[2];
+    // one query group in three steps: S^T, then the online softmax (P^T packed to bf16), then
+    // O^T += V^T P^T
+    auto scores = [&](int i, f32x16 (&sacc)[2]) {
 #pragma unroll
       for (int js = 0; js < 2; ++js) {
         sacc[js] = f32x16{};
 #pragma unroll
         for (int s = 0; s < 4; ++s) Mfma<bf16>::mma(sacc[js], TK::frag(ktile, js * 32, s, lane), qf[i][s]);
       }
+    };
+    auto softmax = [&](int i, bool diag, f32x16 (&sacc)[2], u32x4 (&pb)[2][2]) {
+      const int qi = qg[i] + l32;
       float mloc = -INFINITY;
       if (diag) {
 #pragma unroll
@@ -380,22 +380,25 @@ __global__ __launch_bounds__(THREADS, 3) void attn_fwd64_kernel(const bf16* __re
 #pragma unroll
         for (int r = 0; r < 16; ++r) mloc = fmaxf(mloc, sacc[js][r]);
       mloc = fmaxf(mloc, __shfl_xor(mloc, 32, 64)) * c;
-      const float m_new = fmaxf(m_run[i], mloc);
-      if (__builtin_amdgcn_ballot_w64(m_new > m_run[i]) != 0) {
+      // The running maximum moves only when some row's maximum grew by more than 2^8: below
+      // that, exp2 of the scores minus the older maximum stays below 256 (no overflow; bf16
+      // keeps its relative precision), and the normalisation by the row sum is unchanged.
+      if (__builtin_amdgcn_ballot_w64(mloc > m_run[i] + 8.0f) != 0) {
+        const float m_new = fmaxf(m_run[i], mloc);
         const float alpha = fast_exp2(m_run[i] - m_new);
         o[i][0] *= alpha;
         o[i][1] *= alpha;
         l_run[i] *= alpha;
         m_run[i] = m_new;
       }
-      u32x4 pb[2][2];
+      const float m_use = m_run[i];
       float lsum = 0.0f;
 #pragma unroll
       for (int js = 0; js < 2; ++js) {
         float p[16];
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-          p[r] = fast_exp2(fmaf(sacc[js][r], c, -m_new));
+          p[r] = fast_exp2(fmaf(sacc[js][r], c, -m_use));
           lsum += p[r];
         }
 #pragma unroll
@@ -404,6 +407,8 @@ __global__ __launch_bounds__(THREADS, 3) void attn_fwd64_kernel(const bf16* __re
                             pack_bf16(p[8 * u + 4], p[8 * u + 5]), pack_bf16(p[8 * u + 6], p[8 * u + 7])};
       }
       l_run[i] += lsum;
+    };
+    auto pv = [&](int i, const u32x4 (&pb)[2][2]) {
 #pragma unroll
       for (int js = 0; js < 2; ++js)
 #pragma unroll
@@ -411,6 +416,15 @@ __global__ __launch_bounds__(THREADS, 3) void attn_fwd64_kernel(const bf16* __re
 #pragma unroll
           for (int db = 0; db < 2; ++db)
             Mfma<bf16>::mma(o[i][db], vt_frag(vtile, db * 32, js * 32 + 16 * u, lane), pb[js][u]);
+    };
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      if (key0 > qg[i] + 31 || qg[i] >= T_) continue;  // every key of the tile is after the group
+      f32x16 sacc[2];
+      u32x4 pb[2][2];
+      scores(i, sacc);
+      softmax(i, key0 + 63 > qg[i], sacc, pb);
+      pv(i, pb);
     }
     };
   for (int kt0 = 0; kt0 < ntiles; kt0 += 3) {
