@@ -502,7 +502,10 @@ gpt2_status backward(gpt2_ctx* c, float grad_scale, int acc) {
   const int M = g.M, d = g.d;
   const float s = grad_scale / (float)M;
   // LM head (tied): df = s * dz wte;  dwte = s * dz^T lnf (+ existing when accumulating)
-  STEP(gemm(c, 1, 0, M, d, g.Vp, b.logits, g.Vp, W(c, g.wte), d, EPI_F32, b.dtmp, d, nullptr,
+  // the input gradients that feed a LayerNorm backward (dtmp) are bf16 on the bf16 path, as a
+  // bf16 product's output gradient is in mixed-precision training; fp32 otherwise
+  const int epi_dy = g.bf16 ? EPI_STORE : EPI_F32;
+  STEP(gemm(c, 1, 0, M, d, g.Vp, b.logits, g.Vp, W(c, g.wte), d, epi_dy, b.dtmp, d, nullptr,
             nullptr, nullptr, nullptr, s, 0.0f));
   {
     GemmParams p{};
@@ -528,7 +531,7 @@ gpt2_status backward(gpt2_ctx* c, float grad_scale, int acc) {
       STEP(colsum(c, b.dbig, 4 * d, fc_part(g, b, l)));
     }
     STEP(gemm_dw(c, d, 4 * d, b.ln2[l], b.dbig, G + g.wfc(l), acc));
-    STEP(gemm(c, 1, 1, M, d, 4 * d, b.dbig, 4 * d, W(c, g.wfc(l)), 4 * d, EPI_F32, b.dtmp, d));
+    STEP(gemm(c, 1, 1, M, d, 4 * d, b.dbig, 4 * d, W(c, g.wfc(l)), 4 * d, epi_dy, b.dtmp, d));
     STEP(ln_backward(c, b.resid_mid[l], b.ln2_mean[l], b.ln2_rstd[l], g.ln2g(l), 1, 2 * l + 1));
     // h_mid = h_l + att W_o + b_o ; dres holds dh_mid
     STEP(gemm_dw(c, d, d, b.att[l], b.dres_t, G + g.wo(l), acc));
@@ -537,7 +540,7 @@ gpt2_status backward(gpt2_ctx* c, float grad_scale, int acc) {
                            b.dqkv, b.dsum, c->stream));
     STEP(colsum(c, b.dqkv, 3 * d, qkv_part(g, b, l)));
     STEP(gemm_dw(c, d, 3 * d, b.ln1[l], b.dqkv, G + g.wqkv(l), acc));
-    STEP(gemm(c, 1, 1, M, d, 3 * d, b.dqkv, 3 * d, W(c, g.wqkv(l)), 3 * d, EPI_F32, b.dtmp, d));
+    STEP(gemm(c, 1, 1, M, d, 3 * d, b.dqkv, 3 * d, W(c, g.wqkv(l)), 3 * d, epi_dy, b.dtmp, d));
     STEP(ln_backward(c, b.resid[l], b.ln1_mean[l], b.ln1_rstd[l], g.ln1g(l), 1, 2 * l));
   }
   HIPCHK(launch_embed_bwd(g.B, g.T, d, b.keys, b.dres, G + g.wte, G + g.wpe, acc, b.segpart,

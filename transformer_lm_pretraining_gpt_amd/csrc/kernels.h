@@ -61,9 +61,9 @@ hipError_t launch_attn_bwd(bool is_bf16, int B, int T, int H, int hd, const void
 // y(T) = LN(x) * g + b; mean, rstd (M).
 hipError_t launch_ln_fwd(bool is_bf16, int M, int d, const float* x, const float* g,
                          const float* b, void* y, float* mean, float* rstd, hipStream_t s);
-// dres (fp32, M x d) = (has_dres ? dres : 0) + LN_bwd(dy); dres_t (T) = copy of the new dres.
-// Column partials per row block into part[blk][3][d]: sum dy*xhat, sum dy, sum new dres.
-hipError_t launch_ln_bwd(bool is_bf16, int M, int d, const float* dy, const float* x,
+// dres (fp32, M x d) = (has_dres ? dres : 0) + LN_bwd(dy), dy (T); dres_t (T) = copy of the new
+// dres. Column partials per row block into part[blk][3][d]: sum dy*xhat, sum dy, sum new dres.
+hipError_t launch_ln_bwd(bool is_bf16, int M, int d, const void* dy, const float* x,
                          const float* mean, const float* rstd, const float* g, float* dres,
                          int has_dres, void* dres_t, float* part, int rows_per_block,
                          hipStream_t s);

@@ -20,6 +20,16 @@ constexpr int MAXV = 8;  // float4 vectors per lane: d <= 2048
 constexpr float LN_EPS = 1e-5f;
 
 template <typename T>
+DEV f32x4 load4(const T* src) {
+  if constexpr (sizeof(T) == 4) {
+    return *reinterpret_cast<const f32x4*>(src);
+  } else {
+    const u32x2 u = ld8(src);
+    return f32x4{bf16lo(u[0]), bf16hi(u[0]), bf16lo(u[1]), bf16hi(u[1])};
+  }
+}
+
+template <typename T>
 DEV void store4(T* dst, const float (&v)[4]) {
   if constexpr (sizeof(T) == 2)
     st8(dst, u32x2{pack_bf16(v[0], v[1]), pack_bf16(v[2], v[3])});
@@ -83,7 +93,7 @@ __global__ __launch_bounds__(256) void ln_fwd_kernel(int M, int d, const float* 
 // One block = 4 waves over rows [blk*rpb, blk*rpb + rpb); wave w takes rows w, w+4, ...
 template <typename T, int NV>
 __global__ __launch_bounds__(256) void ln_bwd_kernel(
-    int M, int d, const float* __restrict__ dy, const float* __restrict__ x,
+    int M, int d, const T* __restrict__ dy, const float* __restrict__ x,
     const float* __restrict__ mean, const float* __restrict__ rstd, const float* __restrict__ g,
     float* __restrict__ dres, int has_dres, T* __restrict__ dres_t, float* __restrict__ part,
     int rpb) {
@@ -108,7 +118,7 @@ __global__ __launch_bounds__(256) void ln_bwd_kernel(
       const int v = lane + 64 * k;
       if (v < nv) {
         const f32x4 xv = *reinterpret_cast<const f32x4*>(x + base + 4 * v);
-        dyv[k] = *reinterpret_cast<const f32x4*>(dy + base + 4 * v);
+        dyv[k] = load4<T>(dy + base + 4 * v);
         // the incoming residual gradient is loaded with the row, ahead of the reductions
         dr[k] = has_dres ? *reinterpret_cast<const f32x4*>(dres + base + 4 * v) : f32x4{0, 0, 0, 0};
 #pragma unroll
@@ -278,7 +288,7 @@ hipError_t launch_ln_fwd(bool is_bf16, int M, int d, const float* x, const float
 
 int ln_bwd_blocks(int M, int rows_per_block) { return (M + rows_per_block - 1) / rows_per_block; }
 
-hipError_t launch_ln_bwd(bool is_bf16, int M, int d, const float* dy, const float* x,
+hipError_t launch_ln_bwd(bool is_bf16, int M, int d, const void* dy, const float* x,
                          const float* mean, const float* rstd, const float* g, float* dres,
                          int has_dres, void* dres_t, float* part, int rows_per_block,
                          hipStream_t s) {
@@ -289,10 +299,12 @@ hipError_t launch_ln_bwd(bool is_bf16, int M, int d, const float* dy, const floa
   return with_nv(d, [&](auto nv) {
     constexpr int NV = decltype(nv)::value;
     if (is_bf16)
-      hipLaunchKernelGGL((ln_bwd_kernel<bf16, NV>), grid, dim3(256), lds, s, M, d, dy, x, mean, rstd,
+      hipLaunchKernelGGL((ln_bwd_kernel<bf16, NV>), grid, dim3(256), lds, s, M, d,
+                         static_cast<const bf16*>(dy), x, mean, rstd,
                          g, dres, has_dres, static_cast<bf16*>(dres_t), part, rows_per_block);
     else
-      hipLaunchKernelGGL((ln_bwd_kernel<float, NV>), grid, dim3(256), lds, s, M, d, dy, x, mean, rstd,
+      hipLaunchKernelGGL((ln_bwd_kernel<float, NV>), grid, dim3(256), lds, s, M, d,
+                         static_cast<const float*>(dy), x, mean, rstd,
                          g, dres, has_dres, static_cast<float*>(dres_t), part, rows_per_block);
     return hipGetLastError();
   });
