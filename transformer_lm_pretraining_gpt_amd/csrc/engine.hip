@@ -351,6 +351,9 @@ struct gpt2_ctx {
   Geo g;
   Bufs b;
   hipStream_t stream;
+  // side stream for work off the forward's critical path (the token sort), joined by events
+  hipStream_t side = nullptr;
+  hipEvent_t fork = nullptr, join = nullptr;
   int64_t t = 0;
   bool have_forward = false;
   std::vector<AdamSeg> segs;
@@ -462,7 +465,12 @@ gpt2_status forward(gpt2_ctx* c, const int32_t* tokens, const int32_t* targets, 
   const int M = g.M, d = g.d;
   HIPCHK(launch_embed_fwd(g.B, g.T, d, g.V, tokens, P + g.wte, P + g.wpe, b.resid[0], b.err,
                           c->stream));
-  HIPCHK(launch_token_sort(M, g.V, tokens, b.keys, c->stream));
+  // The token sort (one workgroup, ~150 us) feeds only the embedding backward: it runs on the side
+  // stream beside the forward's kernels, and the end of the forward waits for it.
+  HIPCHK(hipEventRecord(c->fork, c->stream));
+  HIPCHK(hipStreamWaitEvent(c->side, c->fork, 0));
+  HIPCHK(launch_token_sort(M, g.V, tokens, b.keys, c->side));
+  HIPCHK(hipEventRecord(c->join, c->side));
   for (int l = 0; l < g.L; ++l) {
     HIPCHK(launch_ln_fwd(g.bf16, M, d, b.resid[l], P + g.ln1g(l), P + g.ln1b(l), b.ln1[l],
                          b.ln1_mean[l], b.ln1_rstd[l], c->stream));
@@ -492,6 +500,7 @@ gpt2_status forward(gpt2_ctx* c, const int32_t* tokens, const int32_t* targets, 
     HIPCHK(launch_xent(g.bf16, M, g.V, g.Vp, b.logits, targets, b.row_loss, b.err, c->stream));
   }
   HIPCHK(launch_loss_mean(M, b.row_loss, b.loss, loss_user, c->stream));
+  HIPCHK(hipStreamWaitEvent(c->stream, c->join, 0));  // the sort has read the tokens
   return GPT2_OK;
 }
 
@@ -600,7 +609,13 @@ gpt2_status gpt2_init(const gpt2_config* cfg, void* d_arena, size_t arena_bytes,
   c->segs = decay_segments(c->g);
   const Geo& g = c->g;
   Bufs& b = c->b;
-  auto bail = [&](gpt2_status s) { delete c; return s; };
+  auto bail = [&](gpt2_status s) {
+    if (c->fork) hipEventDestroy(c->fork);
+    if (c->join) hipEventDestroy(c->join);
+    if (c->side) hipStreamDestroy(c->side);
+    delete c;
+    return s;
+  };
 #define INITCHK(x)                                                                       \
   do {                                                                                   \
     hipError_t e_ = (x);                                                                 \
@@ -627,6 +642,9 @@ gpt2_status gpt2_init(const gpt2_config* cfg, void* d_arena, size_t arena_bytes,
   b.ncolblocks = coltasks.empty() ? 0 : coltasks.back().block0 + (coltasks.back().n + 63) / 64;
   INITCHK(hipMemcpyAsync(b.coltasks, coltasks.data(), sizeof(ColTask) * coltasks.size(),
                          hipMemcpyHostToDevice, c->stream));
+  INITCHK(hipStreamCreateWithFlags(&c->side, hipStreamNonBlocking));
+  INITCHK(hipEventCreateWithFlags(&c->fork, hipEventDisableTiming));
+  INITCHK(hipEventCreateWithFlags(&c->join, hipEventDisableTiming));
   INITCHK(hipStreamSynchronize(c->stream));
 #undef INITCHK
   *out = c;
@@ -685,6 +703,9 @@ gpt2_status gpt2_check(gpt2_ctx* c) {
 gpt2_status gpt2_destroy(gpt2_ctx* c) {
   if (!c) return fail(GPT2_E_INVALID, "context is NULL");
   for (hipEvent_t e : c->ev) hipEventDestroy(e);
+  if (c->fork) hipEventDestroy(c->fork);
+  if (c->join) hipEventDestroy(c->join);
+  if (c->side) hipStreamDestroy(c->side);
   delete c;
   return GPT2_OK;
 }
