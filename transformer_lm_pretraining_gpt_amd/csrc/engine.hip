@@ -215,9 +215,12 @@ struct Bufs {
   float *row_loss = nullptr, *loss = nullptr;
   int* err = nullptr;
   float* dres = nullptr;
-  void* dres_t = nullptr;
+  // Output gradients that weight-gradient products read on the side stream get a buffer per
+  // producer, so the backward on the main stream never overwrites one still being read:
+  // dres_t per LayerNorm backward (slot k as for the column sums), dbig and dqkv per layer.
+  std::vector<void*> dres_t, dbig, dqkv;
   float* dtmp = nullptr;
-  void *dbig = nullptr, *dqkv = nullptr, *datt = nullptr;
+  void* datt = nullptr;
   float* dsum = nullptr;
   float* colpart = nullptr;      // column-sum partial rows: one slice per reduction of a backward
   ColTask* coltasks = nullptr;   // the reductions of those slices (device table, built at init)
@@ -279,10 +282,13 @@ size_t carve(const Geo& g, uintptr_t base, Bufs& b) {
   b.loss = c.take<float>(4);
   b.err = c.take<int>(4);
   b.dres = c.take<float>(4 * M * d);
-  b.dres_t = c.take<void>(ts * M * d);
+  b.dres_t.resize(2 * g.L + 1);
+  for (auto& p : b.dres_t) p = c.take<void>(ts * M * d);
   b.dtmp = c.take<float>(4 * M * d);
-  b.dbig = c.take<void>(ts * M * 4 * d);
-  b.dqkv = c.take<void>(ts * M * 3 * d);
+  b.dbig.resize(g.L);
+  for (auto& p : b.dbig) p = c.take<void>(ts * M * 4 * d);
+  b.dqkv.resize(g.L);
+  for (auto& p : b.dqkv) p = c.take<void>(ts * M * 3 * d);
   b.datt = c.take<void>(ts * M * d);
   b.dsum = c.take<float>(8 * bht);  // attention backward scratch: 2 floats per (b, h, t)
   const size_t nblk = (size_t)ln_bwd_blocks(g.M, LN_ROWS_PER_BLOCK);
@@ -354,6 +360,8 @@ struct gpt2_ctx {
   // side stream for work off the forward's critical path (the token sort), joined by events
   hipStream_t side = nullptr;
   hipEvent_t fork = nullptr, join = nullptr;
+  // backward: LayerNorm slot k done (2L + 1), dbig and dqkv of layer l written (L each)
+  std::vector<hipEvent_t> ev_ln, ev_dbig, ev_dqkv;
   int64_t t = 0;
   bool have_forward = false;
   std::vector<AdamSeg> segs;
@@ -369,17 +377,19 @@ namespace {
 // Records an event pair around one launch when its family is being timed.
 struct Timed {
   gpt2_ctx* c;
+  hipStream_t s;
   bool on;
-  Timed(gpt2_ctx* c_, int family, double work) : c(c_), on(false) {
+  Timed(gpt2_ctx* c_, int family, double work, hipStream_t s_ = nullptr)
+      : c(c_), s(s_ ? s_ : c_->stream), on(false) {
     if (c->timing_family == family && c->timed < TIMING_CAP) {
       on = true;
-      hipEventRecord(c->ev[2 * c->timed], c->stream);
+      hipEventRecord(c->ev[2 * c->timed], s);
       c->timed_work += work;
     }
   }
   ~Timed() {
     if (on) {
-      hipEventRecord(c->ev[2 * c->timed + 1], c->stream);
+      hipEventRecord(c->ev[2 * c->timed + 1], s);
       ++c->timed;
     }
   }
@@ -413,31 +423,31 @@ gpt2_status gemm(gpt2_ctx* c, int a_kmajor, int b_kmajor, int M, int N, int K, c
 // Weight gradient dW (in x out) = X^T dY over the M rows, X (M x in) and dY (M x out) row-major,
 // written (accumulate = 0) or added (1) into the fp32 gradient at gw.
 gpt2_status gemm_dw(gpt2_ctx* c, int in, int out, const void* X, const void* dY, float* gw,
-                    int accumulate) {
+                    int accumulate, hipStream_t st) {
   const Geo& g = c->g;
   const Split sp = pick_split(g, in, out);
   GemmParams p{};
   p.A = X; p.lda = in; p.B = dY; p.ldb = out;
   p.M = in; p.N = out; p.K = g.M; p.k_split = sp.k_split;
   p.epi = EPI_F32; p.alpha = 1.0f;
-  Timed t1(c, FAM_GEMM, 2.0 * in * out * g.M);
+  Timed t1(c, FAM_GEMM, 2.0 * in * out * g.M, st);
   const int tile = g.bf16 ? TILE_256 : TILE_128;
   if (sp.splits == 1) {
     p.C = gw; p.ldc = out; p.beta = accumulate ? 1.0f : 0.0f;
-    HIPCHK(launch_gemm(g.bf16, 0, 0, tile, 1, 0, p, c->stream));
+    HIPCHK(launch_gemm(g.bf16, 0, 0, tile, 1, 0, p, st));
   } else {
     p.C = c->b.splitk; p.ldc = out; p.c_split_stride = (int64_t)in * out; p.beta = 0.0f;
-    HIPCHK(launch_gemm(g.bf16, 0, 0, tile, sp.splits, 0, p, c->stream));
+    HIPCHK(launch_gemm(g.bf16, 0, 0, tile, sp.splits, 0, p, st));
     HIPCHK(launch_splitk_reduce(c->b.splitk, sp.splits, (int64_t)in * out, in, out, gw, out, 1.0f,
-                                accumulate ? 1.0f : 0.0f, c->stream));
+                                accumulate ? 1.0f : 0.0f, st));
   }
   return GPT2_OK;
 }
 
 // Column partial sums of an (M, N) matrix into `part` (reduced with the others at the end)
-gpt2_status colsum(gpt2_ctx* c, const void* src, int N, float* part) {
+gpt2_status colsum(gpt2_ctx* c, const void* src, int N, float* part, hipStream_t st) {
   const Geo& g = c->g;
-  HIPCHK(launch_colsum_partial(g.bf16, g.M, N, src, N, part, COLSUM_ROWS_PER_BLOCK, c->stream));
+  HIPCHK(launch_colsum_partial(g.bf16, g.M, N, src, N, part, COLSUM_ROWS_PER_BLOCK, st));
   return GPT2_OK;
 }
 
@@ -448,7 +458,8 @@ gpt2_status ln_backward(gpt2_ctx* c, const float* x, const float* mean, const fl
                         int64_t g_off, int has_dres, int k) {
   const Geo& g = c->g;
   HIPCHK(launch_ln_bwd(g.bf16, g.M, g.d, c->b.dtmp, x, mean, rstd, c->b.params + g_off, c->b.dres,
-                       has_dres, c->b.dres_t, ln_part(g, c->b, k), LN_ROWS_PER_BLOCK, c->stream));
+                       has_dres, c->b.dres_t[k], ln_part(g, c->b, k), LN_ROWS_PER_BLOCK,
+                       c->stream));
   return GPT2_OK;
 }
 
@@ -504,54 +515,77 @@ gpt2_status forward(gpt2_ctx* c, const int32_t* tokens, const int32_t* targets, 
   return GPT2_OK;
 }
 
+// The backward runs the chain of input gradients (the critical path) on the main stream and
+// every weight-gradient product (with its split-K sum) and the QKV bias partial sums on the side
+// stream, each waiting for the event of the output gradient it reads. The two streams fill each
+// other's idle CUs (a product's partly filled last round of tiles, the latency-bound attention
+// backward). The main stream joins the side stream before the embedding backward, which adds to
+// the LM head's weight gradient.
 gpt2_status backward(gpt2_ctx* c, float grad_scale, int acc) {
   const Geo& g = c->g;
   Bufs& b = c->b;
   float* G = b.grads;
   const int M = g.M, d = g.d;
   const float s = grad_scale / (float)M;
-  // LM head (tied): df = s * dz wte;  dwte = s * dz^T lnf (+ existing when accumulating)
-  // the input gradients that feed a LayerNorm backward (dtmp) are bf16 on the bf16 path, as a
-  // bf16 product's output gradient is in mixed-precision training; fp32 otherwise
-  const int epi_dy = g.bf16 ? EPI_STORE : EPI_F32;
-  STEP(gemm(c, 1, 0, M, d, g.Vp, b.logits, g.Vp, W(c, g.wte), d, epi_dy, b.dtmp, d, nullptr,
-            nullptr, nullptr, nullptr, s, 0.0f));
+  hipStream_t side = c->side;
+  HIPCHK(hipEventRecord(c->fork, c->stream));  // the logits' gradients (cross-entropy) are done
+  HIPCHK(hipStreamWaitEvent(side, c->fork, 0));
+  // LM head (tied): dwte = s * dz^T lnf (+ existing when accumulating), on the side stream;
+  // df = s * dz wte. The input gradients that feed a LayerNorm backward (dtmp) are bf16 on the
+  // bf16 path, as a bf16 product's output gradient is in mixed-precision training; fp32 otherwise.
   {
     GemmParams p{};
     p.A = b.logits; p.lda = g.Vp; p.B = b.lnf; p.ldb = d;
     p.M = g.Vp; p.N = d; p.K = M; p.k_split = M;
     p.epi = EPI_F32; p.C = G + g.wte; p.ldc = d; p.alpha = s; p.beta = acc ? 1.0f : 0.0f;
-    Timed t(c, FAM_GEMM, 2.0 * g.Vp * d * M);
-    HIPCHK(launch_gemm(g.bf16, 0, 0, pick_tile(g, g.Vp, d), 1, 0, p, c->stream));
+    Timed t(c, FAM_GEMM, 2.0 * g.Vp * d * M, side);
+    HIPCHK(launch_gemm(g.bf16, 0, 0, pick_tile(g, g.Vp, d), 1, 0, p, side));
   }
+  const int epi_dy = g.bf16 ? EPI_STORE : EPI_F32;
+  STEP(gemm(c, 1, 0, M, d, g.Vp, b.logits, g.Vp, W(c, g.wte), d, epi_dy, b.dtmp, d, nullptr,
+            nullptr, nullptr, nullptr, s, 0.0f));
   STEP(ln_backward(c, b.resid[g.L], b.lnf_mean, b.lnf_rstd, g.lnfg, 0, 2 * g.L));
+  HIPCHK(hipEventRecord(c->ev_ln[2 * g.L], c->stream));
   for (int l = g.L - 1; l >= 0; --l) {
-    // h_{l+1} = h_mid + act W_proj + b_proj ; dres holds dh_{l+1}
-    STEP(gemm_dw(c, 4 * d, d, b.act[l], b.dres_t, G + g.wproj(l), acc));
+    // h_{l+1} = h_mid + act W_proj + b_proj: its gradient came from LayerNorm slot kp
+    const int kp = l == g.L - 1 ? 2 * g.L : 2 * (l + 1);
+    void* dh = b.dres_t[kp];
+    HIPCHK(hipStreamWaitEvent(side, c->ev_ln[kp], 0));
+    STEP(gemm_dw(c, 4 * d, d, b.act[l], dh, G + g.wproj(l), acc, side));
     // du = (dh W_proj^T) o GELU'(u); its column sums (the fc bias gradient) come out of the same
     // product's epilogue as one partial row per 128 (or 64) rows when it runs the direct-to-LDS
     // bf16 path, else from a separate pass
     if (fused_colsum(g)) {
-      STEP(gemm(c, 1, 1, M, 4 * d, d, b.dres_t, d, W(c, g.wproj(l)), d, EPI_GELU_BWD, b.dbig,
+      STEP(gemm(c, 1, 1, M, 4 * d, d, dh, d, W(c, g.wproj(l)), d, EPI_GELU_BWD, b.dbig[l],
                 4 * d, nullptr, nullptr, nullptr, b.fc[l], 1.0f, 0.0f, 0, fc_part(g, b, l)));
     } else {
-      STEP(gemm(c, 1, 1, M, 4 * d, d, b.dres_t, d, W(c, g.wproj(l)), d, EPI_GELU_BWD, b.dbig,
+      STEP(gemm(c, 1, 1, M, 4 * d, d, dh, d, W(c, g.wproj(l)), d, EPI_GELU_BWD, b.dbig[l],
                 4 * d, nullptr, nullptr, nullptr, b.fc[l]));
-      STEP(colsum(c, b.dbig, 4 * d, fc_part(g, b, l)));
+      STEP(colsum(c, b.dbig[l], 4 * d, fc_part(g, b, l), c->stream));
     }
-    STEP(gemm_dw(c, d, 4 * d, b.ln2[l], b.dbig, G + g.wfc(l), acc));
-    STEP(gemm(c, 1, 1, M, d, 4 * d, b.dbig, 4 * d, W(c, g.wfc(l)), 4 * d, epi_dy, b.dtmp, d));
+    HIPCHK(hipEventRecord(c->ev_dbig[l], c->stream));
+    HIPCHK(hipStreamWaitEvent(side, c->ev_dbig[l], 0));
+    STEP(gemm_dw(c, d, 4 * d, b.ln2[l], b.dbig[l], G + g.wfc(l), acc, side));
+    STEP(gemm(c, 1, 1, M, d, 4 * d, b.dbig[l], 4 * d, W(c, g.wfc(l)), 4 * d, epi_dy, b.dtmp, d));
     STEP(ln_backward(c, b.resid_mid[l], b.ln2_mean[l], b.ln2_rstd[l], g.ln2g(l), 1, 2 * l + 1));
-    // h_mid = h_l + att W_o + b_o ; dres holds dh_mid
-    STEP(gemm_dw(c, d, d, b.att[l], b.dres_t, G + g.wo(l), acc));
-    STEP(gemm(c, 1, 1, M, d, d, b.dres_t, d, W(c, g.wo(l)), d, EPI_STORE, b.datt, d));
+    HIPCHK(hipEventRecord(c->ev_ln[2 * l + 1], c->stream));
+    // h_mid = h_l + att W_o + b_o
+    void* dm = b.dres_t[2 * l + 1];
+    HIPCHK(hipStreamWaitEvent(side, c->ev_ln[2 * l + 1], 0));
+    STEP(gemm_dw(c, d, d, b.att[l], dm, G + g.wo(l), acc, side));
+    STEP(gemm(c, 1, 1, M, d, d, dm, d, W(c, g.wo(l)), d, EPI_STORE, b.datt, d));
     HIPCHK(launch_attn_bwd(g.bf16, g.B, g.T, g.H, g.hd, b.qkv[l], b.att[l], b.lse[l], b.datt,
-                           b.dqkv, b.dsum, c->stream));
-    STEP(colsum(c, b.dqkv, 3 * d, qkv_part(g, b, l)));
-    STEP(gemm_dw(c, d, 3 * d, b.ln1[l], b.dqkv, G + g.wqkv(l), acc));
-    STEP(gemm(c, 1, 1, M, d, 3 * d, b.dqkv, 3 * d, W(c, g.wqkv(l)), 3 * d, epi_dy, b.dtmp, d));
+                           b.dqkv[l], b.dsum, c->stream));
+    HIPCHK(hipEventRecord(c->ev_dqkv[l], c->stream));
+    HIPCHK(hipStreamWaitEvent(side, c->ev_dqkv[l], 0));
+    STEP(colsum(c, b.dqkv[l], 3 * d, qkv_part(g, b, l), side));
+    STEP(gemm_dw(c, d, 3 * d, b.ln1[l], b.dqkv[l], G + g.wqkv(l), acc, side));
+    STEP(gemm(c, 1, 1, M, d, 3 * d, b.dqkv[l], 3 * d, W(c, g.wqkv(l)), 3 * d, epi_dy, b.dtmp, d));
     STEP(ln_backward(c, b.resid[l], b.ln1_mean[l], b.ln1_rstd[l], g.ln1g(l), 1, 2 * l));
+    HIPCHK(hipEventRecord(c->ev_ln[2 * l], c->stream));
   }
+  HIPCHK(hipEventRecord(c->join, side));
+  HIPCHK(hipStreamWaitEvent(c->stream, c->join, 0));
   HIPCHK(launch_embed_bwd(g.B, g.T, d, b.keys, b.dres, G + g.wte, G + g.wpe, acc, b.segpart,
                           c->stream));
   // every bias and LayerNorm gain/shift gradient from its partial rows, in one launch
@@ -612,6 +646,9 @@ gpt2_status gpt2_init(const gpt2_config* cfg, void* d_arena, size_t arena_bytes,
   auto bail = [&](gpt2_status s) {
     if (c->fork) hipEventDestroy(c->fork);
     if (c->join) hipEventDestroy(c->join);
+    for (auto* v : {&c->ev_ln, &c->ev_dbig, &c->ev_dqkv})
+      for (hipEvent_t e : *v)
+        if (e) hipEventDestroy(e);
     if (c->side) hipStreamDestroy(c->side);
     delete c;
     return s;
@@ -645,6 +682,11 @@ gpt2_status gpt2_init(const gpt2_config* cfg, void* d_arena, size_t arena_bytes,
   INITCHK(hipStreamCreateWithFlags(&c->side, hipStreamNonBlocking));
   INITCHK(hipEventCreateWithFlags(&c->fork, hipEventDisableTiming));
   INITCHK(hipEventCreateWithFlags(&c->join, hipEventDisableTiming));
+  c->ev_ln.assign(2 * g.L + 1, nullptr);
+  c->ev_dbig.assign(g.L, nullptr);
+  c->ev_dqkv.assign(g.L, nullptr);
+  for (auto* v : {&c->ev_ln, &c->ev_dbig, &c->ev_dqkv})
+    for (hipEvent_t& e : *v) INITCHK(hipEventCreateWithFlags(&e, hipEventDisableTiming));
   INITCHK(hipStreamSynchronize(c->stream));
 #undef INITCHK
   *out = c;
@@ -705,6 +747,9 @@ gpt2_status gpt2_destroy(gpt2_ctx* c) {
   for (hipEvent_t e : c->ev) hipEventDestroy(e);
   if (c->fork) hipEventDestroy(c->fork);
   if (c->join) hipEventDestroy(c->join);
+  for (auto* v : {&c->ev_ln, &c->ev_dbig, &c->ev_dqkv})
+    for (hipEvent_t e : *v)
+      if (e) hipEventDestroy(e);
   if (c->side) hipStreamDestroy(c->side);
   delete c;
   return GPT2_OK;
