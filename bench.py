@@ -188,6 +188,10 @@ def main():
                              "achieved": round(rate / 1e9, 1), "unit": unit,
                              "frac": round(rate / 1e9 / HBM_PEAK_GBS, 4)}
         out["kernels"] = fams
+        out["kernels_note"] = ("per family: the sum of each launch's own duration (HIP events); the "
+                               "weight-gradient products run on a second stream beside the "
+                               "backward's input-gradient chain, so the gemm sum exceeds the "
+                               "share of wall time it takes")
 
     if args.copy_calibration:
         src = torch.ones(1 << 28, dtype=torch.float32, device="cuda")
