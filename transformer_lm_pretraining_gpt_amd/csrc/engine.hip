@@ -362,6 +362,8 @@ struct gpt2_ctx {
   hipEvent_t fork = nullptr, join = nullptr;
   // backward: LayerNorm slot k done (2L + 1), dbig and dqkv of layer l written (L each)
   std::vector<hipEvent_t> ev_ln, ev_dbig, ev_dqkv;
+  // AdamW: parameter range r updated (embeddings, layers 0 .. L-1, final LayerNorm: L + 2)
+  std::vector<hipEvent_t> ev_adam;
   int64_t t = 0;
   bool have_forward = false;
   std::vector<AdamSeg> segs;
@@ -474,6 +476,9 @@ gpt2_status forward(gpt2_ctx* c, const int32_t* tokens, const int32_t* targets, 
   Bufs& b = c->b;
   float* P = b.params;
   const int M = g.M, d = g.d;
+  // each parameter range is used once the last AdamW step has updated it (events of the side
+  // stream; recorded already when no update is pending)
+  HIPCHK(hipStreamWaitEvent(c->stream, c->ev_adam[0], 0));
   HIPCHK(launch_embed_fwd(g.B, g.T, d, g.V, tokens, P + g.wte, P + g.wpe, b.resid[0], b.err,
                           c->stream));
   // The token sort (one workgroup, ~150 us) feeds only the embedding backward: it runs on the side
@@ -483,6 +488,7 @@ gpt2_status forward(gpt2_ctx* c, const int32_t* tokens, const int32_t* targets, 
   HIPCHK(launch_token_sort(M, g.V, tokens, b.keys, c->side));
   HIPCHK(hipEventRecord(c->join, c->side));
   for (int l = 0; l < g.L; ++l) {
+    HIPCHK(hipStreamWaitEvent(c->stream, c->ev_adam[1 + l], 0));
     HIPCHK(launch_ln_fwd(g.bf16, M, d, b.resid[l], P + g.ln1g(l), P + g.ln1b(l), b.ln1[l],
                          b.ln1_mean[l], b.ln1_rstd[l], c->stream));
     STEP(gemm(c, 1, 0, M, 3 * d, d, b.ln1[l], d, W(c, g.wqkv(l)), 3 * d, EPI_STORE, b.qkv[l],
@@ -501,6 +507,7 @@ gpt2_status forward(gpt2_ctx* c, const int32_t* tokens, const int32_t* targets, 
     STEP(gemm(c, 1, 0, M, d, 4 * d, b.act[l], 4 * d, W(c, g.wproj(l)), d, EPI_BIAS_RESID,
               b.resid[l + 1], d, P + g.bproj(l), b.resid_mid[l]));
   }
+  HIPCHK(hipStreamWaitEvent(c->stream, c->ev_adam[g.L + 1], 0));
   HIPCHK(launch_ln_fwd(g.bf16, M, d, b.resid[g.L], P + g.lnfg, P + g.lnfb, b.lnf, b.lnf_mean,
                        b.lnf_rstd, c->stream));
   STEP(gemm(c, 1, 1, M, g.Vp, d, b.lnf, d, W(c, g.wte), d, EPI_STORE, b.logits, g.Vp, nullptr,
@@ -528,6 +535,8 @@ gpt2_status backward(gpt2_ctx* c, float grad_scale, int acc) {
   const int M = g.M, d = g.d;
   const float s = grad_scale / (float)M;
   hipStream_t side = c->side;
+  // every AdamW range has landed (a forward normally waited for them already)
+  HIPCHK(hipStreamWaitEvent(c->stream, c->ev_adam[g.L + 1], 0));
   HIPCHK(hipEventRecord(c->fork, c->stream));  // the logits' gradients (cross-entropy) are done
   HIPCHK(hipStreamWaitEvent(side, c->fork, 0));
   // LM head (tied): dwte = s * dz^T lnf (+ existing when accumulating), on the side stream;
@@ -646,7 +655,7 @@ gpt2_status gpt2_init(const gpt2_config* cfg, void* d_arena, size_t arena_bytes,
   auto bail = [&](gpt2_status s) {
     if (c->fork) hipEventDestroy(c->fork);
     if (c->join) hipEventDestroy(c->join);
-    for (auto* v : {&c->ev_ln, &c->ev_dbig, &c->ev_dqkv})
+    for (auto* v : {&c->ev_ln, &c->ev_dbig, &c->ev_dqkv, &c->ev_adam})
       for (hipEvent_t e : *v)
         if (e) hipEventDestroy(e);
     if (c->side) hipStreamDestroy(c->side);
@@ -685,8 +694,10 @@ gpt2_status gpt2_init(const gpt2_config* cfg, void* d_arena, size_t arena_bytes,
   c->ev_ln.assign(2 * g.L + 1, nullptr);
   c->ev_dbig.assign(g.L, nullptr);
   c->ev_dqkv.assign(g.L, nullptr);
-  for (auto* v : {&c->ev_ln, &c->ev_dbig, &c->ev_dqkv})
+  c->ev_adam.assign(g.L + 2, nullptr);
+  for (auto* v : {&c->ev_ln, &c->ev_dbig, &c->ev_dqkv, &c->ev_adam})
     for (hipEvent_t& e : *v) INITCHK(hipEventCreateWithFlags(&e, hipEventDisableTiming));
+  for (hipEvent_t e : c->ev_adam) INITCHK(hipEventRecord(e, c->stream));  // nothing pending
   INITCHK(hipStreamSynchronize(c->stream));
 #undef INITCHK
   *out = c;
@@ -719,10 +730,36 @@ gpt2_status gpt2_adamw_step(gpt2_ctx* c, float lr, float beta1, float beta2, flo
   c->t += 1;
   const double bc1 = 1.0 / (1.0 - pow((double)beta1, (double)c->t));
   const double bc2 = 1.0 / (1.0 - pow((double)beta2, (double)c->t));
-  Timed t(c, FAM_ADAMW, 30.0 * c->g.N);
-  HIPCHK(launch_adamw(c->g.N, c->b.params, c->b.grads, c->b.m, c->b.v, c->b.shadow,
-                      c->b.segs, (int)c->segs.size(), lr, beta1, beta2, eps, weight_decay,
-                      (float)bc1, (float)bc2, c->stream));
+  // Parameter ranges in the order the forward first uses them: the embeddings, layer 0 .. L-1,
+  // the final LayerNorm. Each is updated on the side stream and its event tells the next forward
+  // when that range's weights (and their bf16 copy) are ready, so the updates of later layers
+  // run beside the forward's first layers.
+  const Geo& g = c->g;
+  std::vector<int64_t> cut{0, g.layer0};
+  for (int l = 1; l <= g.L; ++l) cut.push_back(g.lay(l));
+  cut.push_back(g.N);
+  bool aligned = true;
+  for (int64_t x : cut) aligned = aligned && x % 4 == 0;
+  if (!aligned) {
+    Timed t(c, FAM_ADAMW, 30.0 * g.N);
+    HIPCHK(launch_adamw(0, g.N, c->b.params, c->b.grads, c->b.m, c->b.v, c->b.shadow, c->b.segs,
+                        (int)c->segs.size(), lr, beta1, beta2, eps, weight_decay, (float)bc1,
+                        (float)bc2, c->stream));
+    for (hipEvent_t e : c->ev_adam) HIPCHK(hipEventRecord(e, c->stream));
+    return GPT2_OK;
+  }
+  HIPCHK(hipEventRecord(c->fork, c->stream));  // the gradients are final
+  HIPCHK(hipStreamWaitEvent(c->side, c->fork, 0));
+  for (int r = 0; r + 1 < (int)cut.size(); ++r) {
+    const int64_t n = cut[r + 1] - cut[r];
+    {
+      Timed t(c, FAM_ADAMW, 30.0 * n, c->side);
+      HIPCHK(launch_adamw(cut[r], n, c->b.params, c->b.grads, c->b.m, c->b.v, c->b.shadow,
+                          c->b.segs, (int)c->segs.size(), lr, beta1, beta2, eps, weight_decay,
+                          (float)bc1, (float)bc2, c->side));
+    }
+    HIPCHK(hipEventRecord(c->ev_adam[r], c->side));
+  }
   return GPT2_OK;
 }
 
@@ -747,7 +784,7 @@ gpt2_status gpt2_destroy(gpt2_ctx* c) {
   for (hipEvent_t e : c->ev) hipEventDestroy(e);
   if (c->fork) hipEventDestroy(c->fork);
   if (c->join) hipEventDestroy(c->join);
-  for (auto* v : {&c->ev_ln, &c->ev_dbig, &c->ev_dqkv})
+  for (auto* v : {&c->ev_ln, &c->ev_dbig, &c->ev_dqkv, &c->ev_adam})
     for (hipEvent_t e : *v)
       if (e) hipEventDestroy(e);
   if (c->side) hipStreamDestroy(c->side);
@@ -759,6 +796,7 @@ static gpt2_status copy_flat(gpt2_ctx* c, int32_t set, float* dev, float* host, 
   if (!host) return fail(GPT2_E_INVALID, "host buffer is NULL");
   if (n != (size_t)c->g.N) return fail(GPT2_E_INVALID, "n must equal the parameter count");
   HIPCHK(hipStreamSynchronize(c->stream));
+  HIPCHK(hipStreamSynchronize(c->side));  // an AdamW update may still be running there
   if (set)
     HIPCHK(hipMemcpy(dev, host, n * sizeof(float), hipMemcpyHostToDevice));
   else
@@ -824,6 +862,7 @@ gpt2_status gpt2_timing_end(gpt2_ctx* c, double* total_ms, int64_t* launches, do
   if (!total_ms || !launches || !work) return fail(GPT2_E_INVALID, "output pointer is NULL");
   c->timing_family = -1;
   HIPCHK(hipStreamSynchronize(c->stream));
+  HIPCHK(hipStreamSynchronize(c->side));
   double ms = 0.0;
   for (int i = 0; i < c->timed; ++i) {
     float e = 0.0f;

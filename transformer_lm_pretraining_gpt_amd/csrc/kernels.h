@@ -118,9 +118,10 @@ struct AdamSeg {
   int decay;
   int pad;
 };
-hipError_t launch_adamw(int64_t n, float* p, const float* g, float* m, float* v, void* shadow,
-                        const AdamSeg* segs, int nseg, float lr, float b1, float b2, float eps,
-                        float wd, float bc1, float bc2, hipStream_t s);
+// AdamW over elements [begin, begin + n) of the flat arrays (begin and n multiples of 4).
+hipError_t launch_adamw(int64_t begin, int64_t n, float* p, const float* g, float* m, float* v,
+                        void* shadow, const AdamSeg* segs, int nseg, float lr, float b1, float b2,
+                        float eps, float wd, float bc1, float bc2, hipStream_t s);
 hipError_t launch_init_normal(int64_t begin, int64_t count, float* p, uint64_t seed, float std,
                               hipStream_t s);
 hipError_t launch_fill(int64_t count, float* p, float value, hipStream_t s);

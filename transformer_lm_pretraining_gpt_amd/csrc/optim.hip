@@ -21,7 +21,8 @@ namespace {
 
 constexpr int THREADS = 256;
 
-__global__ __launch_bounds__(THREADS) void adamw_kernel(int64_t n4, float* __restrict__ p,
+__global__ __launch_bounds__(THREADS) void adamw_kernel(int64_t begin, int64_t n4,
+                                                        float* __restrict__ p,
                                                         const float* __restrict__ g,
                                                         float* __restrict__ m,
                                                         float* __restrict__ v,
@@ -32,7 +33,7 @@ __global__ __launch_bounds__(THREADS) void adamw_kernel(int64_t n4, float* __res
                                                         float bc2) {
   for (int64_t i = (int64_t)blockIdx.x * THREADS + threadIdx.x; i < n4;
        i += (int64_t)gridDim.x * THREADS) {
-    const int64_t e = 4 * i;
+    const int64_t e = begin + 4 * i;
     // segment holding element e (segments are sorted, the first begins at 0)
     int lo = 0, hi = nseg - 1;
     while (lo < hi) {
@@ -141,12 +142,13 @@ unsigned grid_for(int64_t work) {
 
 }  // namespace
 
-hipError_t launch_adamw(int64_t n, float* p, const float* g, float* m, float* v, void* shadow,
-                        const AdamSeg* segs, int nseg, float lr, float b1, float b2, float eps,
-                        float wd, float bc1, float bc2, hipStream_t s) {
-  if (n % 4) return hipErrorInvalidValue;
+hipError_t launch_adamw(int64_t begin, int64_t n, float* p, const float* g, float* m, float* v,
+                        void* shadow, const AdamSeg* segs, int nseg, float lr, float b1, float b2,
+                        float eps, float wd, float bc1, float bc2, hipStream_t s) {
+  if (n % 4 || begin % 4) return hipErrorInvalidValue;
   const int64_t n4 = n / 4;
-  hipLaunchKernelGGL(adamw_kernel, dim3(grid_for(n4)), dim3(THREADS), 0, s, n4, p, g, m, v,
+  if (n4 == 0) return hipSuccess;
+  hipLaunchKernelGGL(adamw_kernel, dim3(grid_for(n4)), dim3(THREADS), 0, s, begin, n4, p, g, m, v,
                      static_cast<bf16*>(shadow), segs, nseg, lr, b1, b2, eps, wd, bc1, bc2);
   return hipGetLastError();
 }
