@@ -660,34 +660,6 @@ DEV u32x4 pack8(const float* p) {
   return u32x4{pack_bf16(p[0], p[1]), pack_bf16(p[2], p[3]), pack_bf16(p[4], p[5]), pack_bf16(p[6], p[7])};
 }
 
-// Per (batch*head, t): {lse * log2(e), D = sum_d dO O} for the head_dim-64 backward.
-__global__ void attn_dsum64_kernel(const bf16* __restrict__ out, const bf16* __restrict__ dout,
-                                   const float* __restrict__ lse, float2* __restrict__ lsed,
-                                   int T_, int H, int rows) {
-  const int lane = threadIdx.x & 63;
-  const int row = blockIdx.x * (blockDim.x / 64) + (threadIdx.x >> 6);
-  if (row >= rows) return;
-  const int dm = H * 64;
-  const int b = row / T_, t = row % T_;
-  for (int v0 = 0; v0 < dm / 8; v0 += 64) {
-    const int v = v0 + lane;
-    float sum = 0.0f;
-    if (v < dm / 8) {
-      float a[8], g[8];
-      Vec<bf16>::unpack(ld16(out + (int64_t)row * dm + v * 8), a);
-      Vec<bf16>::unpack(ld16(dout + (int64_t)row * dm + v * 8), g);
-#pragma unroll
-      for (int e = 0; e < 8; ++e) sum += a[e] * g[e];
-    }
-#pragma unroll
-    for (int o = 1; o < 8; o <<= 1) sum += __shfl_xor(sum, o, 64);
-    if (v < dm / 8 && (v % 8) == 0) {
-      const int64_t i = ((int64_t)b * H + v / 8) * T_ + t;
-      lsed[i] = make_float2(lse[i] * LOG2E, sum);
-    }
-  }
-}
-
 // dK and dV for 128 keys per block (32 per wave, one key per lane): S = Q K^T and dP = dO V^T
 // with the key's K and V rows as register B operands, then dV^T += dO^T P and dK^T += Q^T dS from
 // the transposed tiles. Query tiles of 64 stream through a three-stage LDS ring with their
@@ -833,9 +805,12 @@ __global__ __launch_bounds__(THREADS, 2) void attn_bwd_dkdv64_kernel(
 // dQ for 256 queries per block (wave w: query groups w and 7 - w, one query per lane):
 // S^T = K Q^T and dP^T = V dO^T with the query's Q and dO rows as register B operands, then
 // dQ^T += K^T dS^T from the transposed K tile. Key tiles stream through a three-stage LDS ring.
+// Each query's D = dO . O is computed here from its own rows and written with lse log2 e as the
+// pair the dK/dV kernel (launched after this one) reads.
 __global__ __launch_bounds__(THREADS, 2) void attn_bwd_dq64_kernel(
-    const bf16* __restrict__ qkv, const bf16* __restrict__ dout, const float2* __restrict__ lsed,
-    bf16* __restrict__ dqkv, int T_, int H) {
+    const bf16* __restrict__ qkv, const bf16* __restrict__ out, const bf16* __restrict__ dout,
+    const float* __restrict__ lse, float2* __restrict__ lsed, bf16* __restrict__ dqkv, int T_,
+    int H) {
   constexpr int NST = 3;
   constexpr int LW = 2 * HeadTile::PER_WAVE;
   __shared__ __attribute__((aligned(1024))) char smem[NST * 16384];
@@ -850,6 +825,7 @@ __global__ __launch_bounds__(THREADS, 2) void attn_bwd_dq64_kernel(
   const bf16* K = Q + dm;
   const bf16* V = Q + 2 * dm;
   const bf16* dO = dout + (int64_t)b * T_ * dm + hh * 64;
+  const bf16* O = out + (int64_t)b * T_ * dm + hh * 64;
   const int q0 = qb * F64_Q;
   const int ntiles = min(T_, q0 + F64_Q) / 64;
 
@@ -864,9 +840,23 @@ __global__ __launch_bounds__(THREADS, 2) void attn_bwd_dq64_kernel(
     const int qi = qg[i] + l32;
     load_row_frags<bf16, 64>(qf[i], Q, ld, qi, T_, h);
     load_row_frags<bf16, 64>(df[i], dO, dm, qi, T_, h);
-    const float2 v = qi < T_ ? lsed[(int64_t)bh * T_ + qi] : make_float2(0.0f, 0.0f);
-    lse2[i] = v.x;
-    dsum[i] = v.y;
+    // D = dO . O over the head's 64 columns: this lane holds 32 of them (half h), the lane 32
+    // apart the other 32
+    u32x4 of[4];
+    load_row_frags<bf16, 64>(of, O, dm, qi, T_, h);
+    float part = 0.0f;
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+      float a[8], g[8];
+      Vec<bf16>::unpack(of[s], a);
+      Vec<bf16>::unpack(df[i][s], g);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) part = fmaf(a[e], g[e], part);
+    }
+    dsum[i] = part + __shfl_xor(part, 32, 64);
+    lse2[i] = qi < T_ ? lse[(int64_t)bh * T_ + qi] * LOG2E : 0.0f;
+    // the {lse log2 e, D} pairs the dK/dV kernel streams with its query tiles
+    if (h == 0 && qi < T_) lsed[(int64_t)bh * T_ + qi] = make_float2(lse2[i], dsum[i]);
     dq[i][0] = dq[i][1] = f32x16{};
   }
   const float c = LOG2E / 8.0f;
@@ -991,16 +981,15 @@ hipError_t bwd_t(int B, int T_, int H, const void* qkv, const void* out, const f
   const int rows = B * T_;
   if constexpr (sizeof(T) == 2 && HD == 64) {
     if (T_ % 64 == 0) {
+      // dQ first: it also writes the {lse log2 e, D} pairs that dK/dV read
       float2* lsed = reinterpret_cast<float2*>(dsum);
-      hipLaunchKernelGGL(attn_dsum64_kernel, dim3((rows + 3) / 4), dim3(256), 0, s,
-                         static_cast<const bf16*>(out), static_cast<const bf16*>(dout), lse, lsed,
-                         T_, H, rows);
+      hipLaunchKernelGGL(attn_bwd_dq64_kernel, dim3(B * H, (T_ + F64_Q - 1) / F64_Q), dim3(THREADS),
+                         0, s, static_cast<const bf16*>(qkv), static_cast<const bf16*>(out),
+                         static_cast<const bf16*>(dout), lse, lsed, static_cast<bf16*>(dqkv), T_,
+                         H);
       hipLaunchKernelGGL(attn_bwd_dkdv64_kernel, dim3(B * H, (T_ + B64_KEYS - 1) / B64_KEYS),
                          dim3(THREADS), 0, s, static_cast<const bf16*>(qkv),
                          static_cast<const bf16*>(dout), lsed, static_cast<bf16*>(dqkv), T_, H);
-      hipLaunchKernelGGL(attn_bwd_dq64_kernel, dim3(B * H, (T_ + F64_Q - 1) / F64_Q), dim3(THREADS),
-                         0, s, static_cast<const bf16*>(qkv), static_cast<const bf16*>(dout), lsed,
-                         static_cast<bf16*>(dqkv), T_, H);
       return hipGetLastError();
     }
   }
