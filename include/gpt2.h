@@ -16,6 +16,9 @@
  *          treinamento": GPT-2 small (12 layers, width 768), micro-batch 16 x 1024, vocabulary
  *          padded from 50257 to 50304 (a multiple of 128); built the nanoGPT way (section
  *          "Ambiente"), i.e. GPT-2's pre-LN block with a tied embedding / LM head.
+ *   [SFT]  same page, section on instruction tuning (SFT): only the assistant's answer and its end
+ *          marker are trained, the prompt is only read; the chat markers take the spare ids of
+ *          the padded vocabulary.
  *
  * Conventions shared by every call
  *   - All calls return gpt2_status. A non-OK status leaves a text in gpt2_last_error() (per
@@ -95,15 +98,19 @@ gpt2_status gpt2_init(const gpt2_config* cfg, void* d_arena, size_t arena_bytes,
                       gpt2_ctx** out);
 
 /* Forward pass and loss ([OBJ]): d_tokens and d_targets are (batch, seq_len) int32 row-major
- * device arrays; targets are the next tokens. Writes the mean cross-entropy over all
- * batch*seq_len positions to *d_loss (one device float) when d_loss is not NULL. Also leaves
- * the per-position losses and the softmax-minus-one-hot gradient of the logits in the arena for
- * gpt2_backward. Ids outside [0, vocab) set the device error word (see gpt2_check). */
+ * device arrays; targets are the next tokens. A target of -1 marks a position that is not trained
+ * ([SFT]): it has loss 0 and contributes no gradient. Writes the mean cross-entropy over the n
+ * trained positions (n = batch*seq_len when no target is -1; 0 when n = 0) to *d_loss (one device
+ * float) when d_loss is not NULL. Also leaves the per-position losses and the softmax-minus-one-hot
+ * gradient of the logits (zero rows where the target is -1) in the arena for gpt2_backward, which
+ * scales the gradient by grad_scale / n. Token ids outside [0, vocab) and targets outside
+ * [0, vocab) other than -1 set the device error word (see gpt2_check). With vocab = vocab_padded
+ * every id of the padded vocabulary is a real token (chat markers on the spare ids, [SFT]). */
 gpt2_status gpt2_forward_loss(gpt2_ctx* ctx, const int32_t* d_tokens, const int32_t* d_targets,
                               float* d_loss);
 
-/* Backward pass ([6ND]) of the most recent forward: gradients of grad_scale * (mean loss) with
- * respect to every parameter, into the flat fp32 gradient buffer. accumulate = 0 overwrites the
+/* Backward pass ([6ND]) of the most recent forward: gradients of grad_scale * (mean loss over the
+ * trained positions) with respect to every parameter, into the flat fp32 gradient buffer. accumulate = 0 overwrites the
  * gradients, 1 adds to them. GPT2_E_STATE if no forward has run since the context was created. */
 gpt2_status gpt2_backward(gpt2_ctx* ctx, float grad_scale, int32_t accumulate);
 

@@ -22,6 +22,12 @@ What is computed, and where the pages state it
 * Backward. Each layer yields a gradient for its input and one for its weights ("Pré-treinar um
   LLM", paragraph deriving the 6ND count). Everything below is plain reverse-mode differentiation
   of the forward, written out formula by formula.
+* Positions that are not trained. A target of -1 marks a position whose next token is only read:
+  it gets no loss and no gradient, and the loss is the mean over the other positions (0, with zero
+  gradient, when there are none). The instruction-tuning run on the first page trains only the
+  assistant's answer and its end marker ("Criei GPT-2 do zero com uma RTX 4090", section on SFT,
+  list item on training only the answer); its chat markers reuse the spare ids of the padded
+  vocabulary (same list), which a configuration with vocab = vocab_padded makes real columns.
 * AdamW. Moments m and v per parameter (same page, paragraph on memory), bias-corrected, with
   decay decoupled from the gradient and scaled by the learning rate; decay applies to 2-D tensors
   only.
@@ -321,15 +327,33 @@ def _lm_chunk_rows(cfg: Config, max_elems: int = 1 << 25) -> int:
     return max(1, min(cfg.rows, max_elems // cfg.vocab_padded))
 
 
+IGNORE = -1  # target of a position that is not trained
+
+
+def trained_count(y: np.ndarray) -> int:
+    """Number of positions whose target is not IGNORE."""
+    return int(np.count_nonzero(np.asarray(y).reshape(-1) != IGNORE))
+
+
+def mean_loss(rows: np.ndarray, y: np.ndarray) -> float:
+    """Mean of the per-row losses over the trained positions; 0 when there are none."""
+    keep = np.asarray(y).reshape(-1) != IGNORE
+    n = int(np.count_nonzero(keep))
+    return float(rows[keep].sum() / n) if n else 0.0
+
+
 def lm_head_loss(f: np.ndarray, wte: np.ndarray, y: np.ndarray, cfg: Config, tally=None,
                  want_grad: bool = True):
-    """Logits z = f @ wte^T with the padded columns at -inf; per-row loss = logsumexp(z) - z[y].
+    """Logits z = f @ wte^T with the padded columns at -inf; per-row loss = logsumexp(z) - z[y],
+    and 0 on rows whose target is IGNORE.
 
     Returns (row_losses (M,), df (M, d) or None, dwte (Vp, d) or None), where the gradients are
-    those of the MEAN loss: dz = (softmax(z) - onehot(y)) / M, df = dz @ wte, dwte = dz^T @ f.
+    those of the MEAN loss over the n trained rows: dz = (softmax(z) - onehot(y)) / n on those rows
+    and 0 on the others, df = dz @ wte, dwte = dz^T @ f.
     """
     M, V = cfg.rows, cfg.vocab
     yf = y.reshape(-1)
+    n = trained_count(yf)
     rows = np.empty(M)
     df = np.empty_like(f) if want_grad else None
     dwte = np.zeros_like(wte) if want_grad else None
@@ -340,11 +364,15 @@ def lm_head_loss(f: np.ndarray, wte: np.ndarray, y: np.ndarray, cfg: Config, tal
         z[:, V:] = -np.inf
         zmax = z.max(axis=1, keepdims=True)
         lse = zmax[:, 0] + np.log(np.exp(z - zmax).sum(axis=1))
-        rows[lo:hi] = lse - z[np.arange(hi - lo), yf[lo:hi]]
+        yc = yf[lo:hi]
+        keep = yc != IGNORE
+        r = np.arange(hi - lo)
+        rows[lo:hi] = np.where(keep, lse - z[r, np.where(keep, yc, 0)], 0.0)
         if want_grad:
             dz = np.exp(z - lse[:, None])
-            dz[np.arange(hi - lo), yf[lo:hi]] -= 1.0
-            dz /= M
+            dz[r[keep], yc[keep]] -= 1.0
+            dz[~keep] = 0.0
+            dz /= max(n, 1)
             df[lo:hi] = _mm(dz, wte, tally, "bwd")
             dwte += _mm(dz.T, f[lo:hi], tally, "bwd")
     return rows, df, dwte
@@ -372,11 +400,12 @@ def forward(params: np.ndarray, x: np.ndarray, y: np.ndarray, cfg: Config, tally
         h, _ = block_forward(h, P, l, cfg, tally, "fwd")
     f, _, _ = layernorm(h, _f64(P["lnf.g"]), _f64(P["lnf.b"]))
     rows, _, _ = lm_head_loss(f, _f64(P["wte"]), y, cfg, tally, want_grad=False)
-    return float(rows.mean()), rows
+    return mean_loss(rows, y), rows
 
 
 def loss_and_grad(params: np.ndarray, x: np.ndarray, y: np.ndarray, cfg: Config, tally=None):
-    """Mean loss, per-row losses and the float64 flat gradient of the mean loss."""
+    """Mean loss (over the trained positions), per-row losses and the float64 flat gradient of the
+    mean loss."""
     P = unpack(params, cfg)
     grad = np.zeros(param_count(cfg), dtype=np.float64)
     G = unpack(grad, cfg)
@@ -398,7 +427,7 @@ def loss_and_grad(params: np.ndarray, x: np.ndarray, y: np.ndarray, cfg: Config,
     dh3 = dh.reshape(cfg.batch, cfg.seq_len, cfg.d_model)
     np.add.at(G["wte"], x.reshape(-1), dh)
     G["wpe"] += dh3.sum(axis=0)
-    return float(rows.mean()), rows, grad
+    return mean_loss(rows, y), rows, grad
 
 
 def adamw_update(p, g, m, v, t: int, lr: float, beta1: float, beta2: float, eps: float,

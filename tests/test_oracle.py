@@ -235,9 +235,11 @@ def test_causality_of_the_loss():
 
 # ------------------------------------------------------------------------------ brute force
 
-def _fd_check(cfg, seed):
+def _fd_check(cfg, seed, masked=False):
     p = random_params(cfg, seed=seed)
     x, y = tokens(cfg, seed=seed + 1)
+    if masked:
+        y = S.chat_mask(y, seed + 3, prompt_mean=8, answer_mean=8)
     loss, _, g = O.loss_and_grad(p, x, y, cfg)
     rng = np.random.default_rng(seed + 2)
     h = 1e-5
@@ -294,7 +296,7 @@ def _torch_step(p_np, x, y, cfg):
     z = f @ P["wte"].T
     mask = torch.arange(cfg.vocab_padded) >= cfg.vocab
     z = z.masked_fill(mask, float("-inf"))
-    loss = F.cross_entropy(z.reshape(-1, cfg.vocab_padded), yt.reshape(-1))
+    loss = F.cross_entropy(z.reshape(-1, cfg.vocab_padded), yt.reshape(-1), ignore_index=-1)
     loss.backward()
     return loss.item(), p.grad.numpy()
 
@@ -311,6 +313,64 @@ def test_matches_torch_functional_autograd(cfg):
         ref = tg[off:off + n]
         err = np.abs(g[off:off + n] - ref).max()
         assert err <= 1e-10 * max(np.abs(ref).max(), 1e-30), name
+
+
+# ------------------------------------------------------------------------------ untrained positions
+
+def _chat(cfg, seed):
+    x, y = tokens(cfg, seed=seed)
+    return x, y, S.chat_mask(y, seed + 100, prompt_mean=8, answer_mean=8)
+
+
+def test_masked_loss_is_mean_over_trained_rows():
+    """The forward never reads the targets except to pick z[y]: with some targets at -1 the other
+    rows keep exactly their losses, the ignored rows report 0 and the loss is the mean over the
+    trained rows."""
+    cfg = TINY_PAD
+    p = random_params(cfg, seed=7)
+    x, y, ym = _chat(cfg, 8)
+    keep = ym.reshape(-1) != O.IGNORE
+    assert 0 < keep.sum() < keep.size
+    _, rows = O.forward(p, x, y, cfg)
+    loss_m, rows_m = O.forward(p, x, ym, cfg)
+    assert np.array_equal(rows_m[keep], rows[keep]) and np.all(rows_m[~keep] == 0.0)
+    assert loss_m == pytest.approx(rows[keep].mean(), rel=1e-13)
+
+
+def test_finite_differences_masked_targets():
+    _fd_check(TINY_PAD, 30, masked=True)
+
+
+@pytest.mark.parametrize("cfg", [TINY_PAD, SMALL_HD64])
+def test_masked_targets_match_torch_ignore_index(cfg):
+    """torch's cross_entropy with ignore_index = -1 averages over the other positions."""
+    p = random_params(cfg, seed=15, std=0.2)
+    x, _, ym = _chat(cfg, 16)
+    loss, _, g = O.loss_and_grad(p, x, ym, cfg)
+    tl, tg = _torch_step(p, x, ym, cfg)
+    assert abs(loss - tl) <= 1e-12 * abs(tl)
+    assert np.abs(g - tg).max() <= 1e-10 * np.abs(tg).max()
+
+
+def test_every_position_ignored():
+    """No trained position: loss 0 and an all-zero gradient (the reading taken where a mean over
+    nothing is undefined)."""
+    cfg = TINY_PAD
+    p = random_params(cfg, seed=17)
+    x, y = tokens(cfg, seed=18)
+    loss, rows, g = O.loss_and_grad(p, x, np.full_like(y, O.IGNORE), cfg)
+    assert loss == 0.0 and np.all(rows == 0.0) and np.all(g == 0.0)
+
+
+def test_chat_mask_spans():
+    """The synthetic chat mask starts each sequence with a prompt and alternates spans."""
+    y = np.arange(4 * 300, dtype=np.int32).reshape(4, 300)
+    m = S.chat_mask(y, 3, prompt_mean=10, answer_mean=20)
+    assert np.all(m[:, 0] == -1)
+    kept = m != -1
+    assert np.array_equal(m[kept], y[kept])
+    frac = 1.0 - kept.mean()
+    assert 0.2 < frac < 0.5
 
 
 def test_full_step_consistency():

@@ -279,7 +279,7 @@ size_t carve(const Geo& g, uintptr_t base, Bufs& b) {
   b.lnf_rstd = c.take<float>(4 * M);
   b.logits = c.take<void>(ts * M * (size_t)g.Vp);
   b.row_loss = c.take<float>(4 * M);
-  b.loss = c.take<float>(4);
+  b.loss = c.take<float>(8);  // mean loss, 1 / (number of trained positions)
   b.err = c.take<int>(4);
   b.dres = c.take<float>(4 * M * d);
   b.dres_t.resize(2 * g.L + 1);
@@ -408,13 +408,14 @@ gpt2_status gemm(gpt2_ctx* c, int a_kmajor, int b_kmajor, int M, int N, int K, c
                  int64_t lda, const void* B, int64_t ldb, int epi, void* C, int64_t ldc,
                  const float* bias = nullptr, const float* resid = nullptr, void* C2 = nullptr,
                  const void* aux = nullptr, float alpha = 1.0f, float beta = 0.0f, int tag = 0,
-                 float* colsum = nullptr) {
+                 float* colsum = nullptr, const float* alpha_scale = nullptr) {
   GemmParams p{};
   p.A = A; p.lda = lda; p.B = B; p.ldb = ldb;
   p.M = M; p.N = N; p.K = K; p.k_split = K;
   p.epi = epi; p.C = C; p.ldc = ldc; p.c_split_stride = 0;
   p.C2 = C2; p.bias = bias; p.resid = resid; p.aux = aux; p.alpha = alpha; p.beta = beta;
   p.colsum = colsum;
+  p.alpha_scale = alpha_scale;
   const double fl = 2.0 * M * N * K;
   Timed t1(c, FAM_GEMM, fl);
   Timed t0(c, tag == 1 ? FAM_LMHEAD : -2, fl);
@@ -517,7 +518,7 @@ gpt2_status forward(gpt2_ctx* c, const int32_t* tokens, const int32_t* targets, 
     Timed t(c, FAM_XENT, bytes);
     HIPCHK(launch_xent(g.bf16, M, g.V, g.Vp, b.logits, targets, b.row_loss, b.err, c->stream));
   }
-  HIPCHK(launch_loss_mean(M, b.row_loss, b.loss, loss_user, c->stream));
+  HIPCHK(launch_loss_mean(M, b.row_loss, targets, b.loss, loss_user, c->stream));
   HIPCHK(hipStreamWaitEvent(c->stream, c->join, 0));  // the sort has read the tokens
   return GPT2_OK;
 }
@@ -533,26 +534,29 @@ gpt2_status backward(gpt2_ctx* c, float grad_scale, int acc) {
   Bufs& b = c->b;
   float* G = b.grads;
   const int M = g.M, d = g.d;
-  const float s = grad_scale / (float)M;
+  // the LM-head gradient products scale by grad_scale / n, n = the number of trained positions
+  // (all M unless targets are -1), which the loss-mean kernel left on the device
+  const float* inv_n = b.loss + 1;
   hipStream_t side = c->side;
   // every AdamW range has landed (a forward normally waited for them already)
   HIPCHK(hipStreamWaitEvent(c->stream, c->ev_adam[g.L + 1], 0));
   HIPCHK(hipEventRecord(c->fork, c->stream));  // the logits' gradients (cross-entropy) are done
   HIPCHK(hipStreamWaitEvent(side, c->fork, 0));
-  // LM head (tied): dwte = s * dz^T lnf (+ existing when accumulating), on the side stream;
-  // df = s * dz wte. The input gradients that feed a LayerNorm backward (dtmp) are bf16 on the
+  // LM head (tied), s = grad_scale / n: dwte = s * dz^T lnf (+ existing when accumulating), on
+  // the side stream; df = s * dz wte. The input gradients that feed a LayerNorm backward (dtmp) are bf16 on the
   // bf16 path, as a bf16 product's output gradient is in mixed-precision training; fp32 otherwise.
   {
     GemmParams p{};
     p.A = b.logits; p.lda = g.Vp; p.B = b.lnf; p.ldb = d;
     p.M = g.Vp; p.N = d; p.K = M; p.k_split = M;
-    p.epi = EPI_F32; p.C = G + g.wte; p.ldc = d; p.alpha = s; p.beta = acc ? 1.0f : 0.0f;
+    p.epi = EPI_F32; p.C = G + g.wte; p.ldc = d; p.alpha = grad_scale; p.beta = acc ? 1.0f : 0.0f;
+    p.alpha_scale = inv_n;
     Timed t(c, FAM_GEMM, 2.0 * g.Vp * d * M, side);
     HIPCHK(launch_gemm(g.bf16, 0, 0, pick_tile(g, g.Vp, d), 1, 0, p, side));
   }
   const int epi_dy = g.bf16 ? EPI_STORE : EPI_F32;
   STEP(gemm(c, 1, 0, M, d, g.Vp, b.logits, g.Vp, W(c, g.wte), d, epi_dy, b.dtmp, d, nullptr,
-            nullptr, nullptr, nullptr, s, 0.0f));
+            nullptr, nullptr, nullptr, grad_scale, 0.0f, 0, nullptr, inv_n));
   STEP(ln_backward(c, b.resid[g.L], b.lnf_mean, b.lnf_rstd, g.lnfg, 0, 2 * g.L));
   HIPCHK(hipEventRecord(c->ev_ln[2 * g.L], c->stream));
   for (int l = g.L - 1; l >= 0; --l) {
@@ -680,7 +684,7 @@ gpt2_status gpt2_init(const gpt2_config* cfg, void* d_arena, size_t arena_bytes,
   INITCHK(launch_fill(g.N, b.v, 0.0f, c->stream));
   if (g.bf16) INITCHK(launch_cast_bf16(g.N, b.params, b.shadow, c->stream));
   INITCHK(hipMemsetAsync(b.err, 0, sizeof(int), c->stream));
-  INITCHK(hipMemsetAsync(b.loss, 0, sizeof(float), c->stream));
+  INITCHK(hipMemsetAsync(b.loss, 0, 2 * sizeof(float), c->stream));
   INITCHK(hipMemcpyAsync(b.segs, c->segs.data(), sizeof(AdamSeg) * c->segs.size(),
                          hipMemcpyHostToDevice, c->stream));
   const std::vector<ColTask> coltasks = col_tasks(g, b);
@@ -773,7 +777,7 @@ gpt2_status gpt2_check(gpt2_ctx* c) {
     HIPCHK(hipMemcpy(c->b.err, &zero, sizeof(int), hipMemcpyHostToDevice));
     std::string what;
     if (err & ERR_TOKEN_RANGE) what += "token id outside [0, vocab); ";
-    if (err & ERR_TARGET_RANGE) what += "target id outside [0, vocab); ";
+    if (err & ERR_TARGET_RANGE) what += "target id outside [0, vocab) and not -1; ";
     return fail(GPT2_E_DEVICE, what);
   }
   return GPT2_OK;

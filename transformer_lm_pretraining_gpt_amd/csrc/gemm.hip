@@ -189,6 +189,7 @@ DEV void epilogue(const f32x16 (&acc)[MB][NB], const GemmParams& p, int row0, in
 
 template <typename T, int AK, int BKM, int BM, int BN, int TAG>
 __global__ __launch_bounds__(THREADS) void gemm_kernel(GemmParams p) {
+  if (p.alpha_scale) p.alpha *= *p.alpha_scale;
   constexpr int WM = BM / 2, WN = BN / 2;
   constexpr int MB = WM / 32, NB = WN / 32;
   constexpr int KT = ROWB / (int)sizeof(T);
@@ -584,6 +585,10 @@ DEV void slab_mma_next(f32x16 (&acc)[MB][NB], u32x4 (&fa)[MB], u32x4 (&fb)[NB], 
 // first and stream in while the finished tile is written out through the free stage.
 template <int AK, int BKM, int BM, int BN, int RB, int NSTAGE, int MINB, int TAG, int NW = 4>
 __global__ __launch_bounds__(64 * NW, MINB) void gemm_dma_kernel(GemmParams p) {
+  // a device-side scale of alpha, read before any of the pipeline's loads is in flight
+  if (p.alpha_scale)
+    p.alpha *= __builtin_bit_cast(
+        float, __builtin_amdgcn_readfirstlane(__builtin_bit_cast(int, *p.alpha_scale)));
   // NW waves in a 2 x NW/2 grid over the block tile
   constexpr int WGN = NW / 2;
   constexpr int WM = BM / 2, WN = BN / WGN;

@@ -29,6 +29,9 @@ struct GemmParams {
   const float* resid;
   const void* aux;
   float alpha, beta;
+  // when set, alpha is multiplied by this device scalar (read once per block): the loss scale
+  // 1 / (number of trained positions) that only the device knows
+  const float* alpha_scale;
   // EPI_GELU_BWD on the direct-to-LDS path only: when set, column sums of the output over each
   // 128-row block of a wave tile go to colsum[(row / 128) * N + col] (fp32, before rounding)
   float* colsum;
@@ -94,12 +97,16 @@ hipError_t launch_colsum_reduce3(const float* part, int nparts, int64_t stride, 
                                  hipStream_t s);
 
 // ------------------------------------------------------------------------------ loss
-// logits (M, Vp) T, overwritten by softmax - onehot (pad columns 0); row_loss (M).
+// Target id of a position that is not trained (no loss, zero gradient).
+constexpr int32_t TARGET_IGNORE = -1;
+// logits (M, Vp) T, overwritten by softmax - onehot (pad columns 0); row_loss (M). Rows whose
+// target is TARGET_IGNORE get loss 0 and an all-zero gradient row.
 hipError_t launch_xent(bool is_bf16, int M, int V, int Vp, void* logits, const int32_t* targets,
                        float* row_loss, int* err, hipStream_t s);
-// loss_out[0] = mean(row_loss); also copies to loss_user if not null.
-hipError_t launch_loss_mean(int M, const float* row_loss, float* loss_out, float* loss_user,
-                            hipStream_t s);
+// With n the number of targets other than TARGET_IGNORE: loss_out[0] = sum(row_loss) / n and
+// loss_out[1] = 1 / n (both 0 when n = 0); loss_out[0] is also copied to loss_user if not null.
+hipError_t launch_loss_mean(int M, const float* row_loss, const int32_t* targets, float* loss_out,
+                            float* loss_user, hipStream_t s);
 
 // ------------------------------------------------------------------------------ embedding
 hipError_t launch_embed_fwd(int B, int T, int d, int V, const int32_t* tokens, const float* wte,

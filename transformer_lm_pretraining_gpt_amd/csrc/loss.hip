@@ -7,9 +7,15 @@
 //
 // One block of 1024 threads per row reads the row once into registers (16-byte vectors), forms the max, the sum
 // of exponentials and the log-sum-exp, writes the per-row loss lse - z[y], and overwrites the row
-// in place with softmax(z) - onehot(y) (zeros in the padded columns). The 1/M mean and the
+// in place with softmax(z) - onehot(y) (zeros in the padded columns). The mean's 1/n and the
 // backward's grad_scale are applied later, as the alpha of the LM-head gradient products, so no
 // probability matrix is ever written besides this in-place gradient.
+//
+// Positions whose target is -1 are not trained (loss 0, gradient row 0) and the loss is the mean
+// over the others: the instruction-tuning run trains only the assistant's answer and its end
+// marker, the prompt being only read ("Criei GPT-2 do zero com uma RTX 4090", section on SFT, list
+// item on training only the answer). Its chat markers reuse the spare ids of the padded vocabulary
+// (same list), which a configuration with vocab = vocab_padded makes real columns.
 #include <math.h>
 
 #include "common.h"
@@ -69,6 +75,12 @@ __global__ __launch_bounds__(THREADS, 8) void xent_kernel(int V, int Vp, T* __re
   const int nvec = Vp / VE;
   const int nfull = V / VE;  // vectors with no padded column
   int y = targets[row];
+  if (y == TARGET_IGNORE) {
+    // a position that is not trained: no loss, a zero gradient row, the logits are not read
+    if (tid == 0) row_loss[row] = 0.0f;
+    for (int v = tid; v < nvec; v += THREADS) st16(z + v * VE, u32x4{0, 0, 0, 0});
+    return;
+  }
   if (y < 0 || y >= V) {
     if (tid == 0) atomicOr(err, ERR_TARGET_RANGE);
     y = 0;  // keep the reads in bounds; the flagged result is not used
@@ -127,18 +139,32 @@ __global__ __launch_bounds__(THREADS, 8) void xent_kernel(int V, int Vp, T* __re
   }
 }
 
+// Mean over the trained positions (ignored rows hold loss 0), and the matching gradient scale.
 __global__ __launch_bounds__(256) void loss_mean_kernel(int M, const float* __restrict__ rows,
+                                                        const int32_t* __restrict__ targets,
                                                         float* __restrict__ out,
                                                         float* __restrict__ out_user) {
   __shared__ float sh[4];
+  __shared__ int shn[4];
   float s = 0.0f;
-  for (int i = threadIdx.x; i < M; i += 256) s += rows[i];
+  int n = 0;
+  for (int i = threadIdx.x; i < M; i += 256) {
+    s += rows[i];
+    n += targets[i] != TARGET_IGNORE;
+  }
   s = wave_sum(s);
-  if ((threadIdx.x & 63) == 0) sh[threadIdx.x >> 6] = s;
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) n += __shfl_xor(n, o, 64);
+  if ((threadIdx.x & 63) == 0) {
+    sh[threadIdx.x >> 6] = s;
+    shn[threadIdx.x >> 6] = n;
+  }
   __syncthreads();
   if (threadIdx.x == 0) {
-    const float mean = (((sh[0] + sh[1]) + sh[2]) + sh[3]) / (float)M;
+    const int cnt = shn[0] + shn[1] + shn[2] + shn[3];
+    const float mean = cnt > 0 ? (((sh[0] + sh[1]) + sh[2]) + sh[3]) / (float)cnt : 0.0f;
     out[0] = mean;
+    out[1] = cnt > 0 ? 1.0f / (float)cnt : 0.0f;
     if (out_user) out_user[0] = mean;
   }
 }
@@ -159,8 +185,9 @@ hipError_t launch_xent(bool is_bf16, int M, int V, int Vp, void* logits, const i
   return hipGetLastError();
 }
 
-hipError_t launch_loss_mean(int M, const float* row_loss, float* loss_out, float* loss_user,
-                            hipStream_t s) {
-  hipLaunchKernelGGL(loss_mean_kernel, dim3(1), dim3(256), 0, s, M, row_loss, loss_out, loss_user);
+hipError_t launch_loss_mean(int M, const float* row_loss, const int32_t* targets, float* loss_out,
+                            float* loss_user, hipStream_t s) {
+  hipLaunchKernelGGL(loss_mean_kernel, dim3(1), dim3(256), 0, s, M, row_loss, targets, loss_out,
+                     loss_user);
   return hipGetLastError();
 }

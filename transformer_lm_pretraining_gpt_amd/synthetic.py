@@ -60,3 +60,26 @@ def tokens_for(kind: str, batch: int, seq_len: int, vocab: int, seed: int, windo
 def normal_vector(n: int, seed: int, std: float = 0.02, dtype=np.float32) -> np.ndarray:
     """n draws of N(0, std^2) from ``numpy.random.default_rng(seed)``."""
     return (np.random.default_rng(seed).standard_normal(n) * std).astype(dtype)
+
+
+def chat_mask(y: np.ndarray, seed: int, prompt_mean: int = 48, answer_mean: int = 96) -> np.ndarray:
+    """A copy of the targets y (B, T) with the positions of synthetic prompts set to -1.
+
+    Stands in for chat data in which only the assistant's answers are trained ("Criei GPT-2 do zero
+    com uma RTX 4090", section on SFT; the chat corpus it uses is not available here): each
+    sequence alternates prompt and answer spans, starting with a prompt, with span lengths drawn
+    uniformly from [1, 2 * mean - 1] by ``numpy.random.default_rng(seed)``.
+    """
+    rng = np.random.default_rng(seed)
+    out = np.array(y, dtype=np.int32, copy=True)
+    B, T = out.shape
+    for b in range(B):
+        t, prompt = 0, True
+        while t < T:
+            mean = prompt_mean if prompt else answer_mean
+            n = int(rng.integers(1, 2 * mean))
+            if prompt:
+                out[b, t:t + n] = -1
+            t += n
+            prompt = not prompt
+    return out
