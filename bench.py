@@ -72,6 +72,58 @@ def cpu_baseline(model, ocfg, x, y):
                       f"the bench batch; {dt:.1f} s"}
 
 
+def _timed(torch, fn, reps):
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    ev0.record()
+    for r in range(reps):
+        fn(r)
+    ev1.record()
+    torch.cuda.synchronize()
+    return ev0.elapsed_time(ev1) / reps
+
+
+def variants(model, torch, S, xs, ys, warmup, nwin, M):
+    """Two variants of the timed step on the same windows:
+    * sft_masked_targets: targets of synthetic prompt spans set to -1 (not trained), the rest as
+      in the headline step; tokens/s counts every position processed;
+    * grad_accum_32: one AdamW step per 32 micro-batches (forward + backward with accumulate = 1
+      and grad_scale = 1/32), the pages' regime of about 0.5M tokens per optimiser step."""
+    res = {}
+    loss = torch.zeros(1, dtype=torch.float32, device="cuda")
+    yms = [torch.from_numpy(S.chat_mask(y.cpu().numpy(), 100 + i)).cuda() for i, y in enumerate(ys)]
+    frac = float(sum((y == -1).sum().item() for y in yms)) / (M * len(yms))
+
+    def masked(r):
+        i = warmup + r % (nwin - warmup)
+        model.forward_loss(xs[i], yms[i], loss)
+        model.backward(1.0, False)
+        model.adamw_step(6e-4, 0.9, 0.95, 1e-8, 0.1)
+
+    masked(0)
+    ms = _timed(torch, masked, 10)
+    model.check()
+    res["sft_masked_targets"] = {"ms_per_step": round(ms, 3), "tokens_per_s": round(M / (ms / 1e3), 1),
+                                 "ignored_fraction": round(frac, 4)}
+
+    acc = 32
+
+    def accum(r):
+        for k in range(acc):
+            i = warmup + (r * acc + k) % (nwin - warmup)
+            model.forward_loss(xs[i], ys[i], loss)
+            model.backward(1.0 / acc, k > 0)
+        model.adamw_step(6e-4, 0.9, 0.95, 1e-8, 0.1)
+
+    accum(0)
+    ms = _timed(torch, accum, 2)
+    model.check()
+    res["grad_accum_32"] = {"ms_per_optimizer_step": round(ms, 2),
+                            "tokens_per_optimizer_step": acc * M,
+                            "tokens_per_s": round(acc * M / (ms / 1e3), 1)}
+    return res
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -80,6 +132,8 @@ def main():
     ap.add_argument("--workload", default="gpt2_124m")
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle's cpu_baseline leg")
     ap.add_argument("--no-breakdown", action="store_true", help="skip per-family kernel timing")
+    ap.add_argument("--no-variants", action="store_true",
+                    help="skip the masked-target and 32x gradient-accumulation variants")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run one plain elementwise copy of 1 GiB (read 1 GiB, write 1 GiB): "
                          "the reference dispatch that scales HBM byte counters")
@@ -192,6 +246,10 @@ def main():
                                "weight-gradient products run on a second stream beside the "
                                "backward's input-gradient chain, so the gemm sum exceeds the "
                                "share of wall time it takes")
+
+    # ---- variants of the step (separate timings, not part of value) ----
+    if not args.no_variants:
+        out["variants"] = variants(model, torch, S, xs, ys, args.warmup, nwin, M)
 
     if args.copy_calibration:
         src = torch.ones(1 << 28, dtype=torch.float32, device="cuda")
