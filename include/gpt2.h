@@ -114,6 +114,15 @@ gpt2_status gpt2_forward_loss(gpt2_ctx* ctx, const int32_t* d_tokens, const int3
  * gradients, 1 adds to them. GPT2_E_STATE if no forward has run since the context was created. */
 gpt2_status gpt2_backward(gpt2_ctx* ctx, float grad_scale, int32_t accumulate);
 
+/* Global-norm gradient clipping, for a training loop that wants it (the pages set no threshold):
+ * norm = sqrt(sum of g^2) over the whole flat gradient, then every gradient is multiplied by
+ * max_norm / (norm + 1e-6) when that factor is below 1 (the rule of torch.nn.utils.
+ * clip_grad_norm_). Asynchronous on the context's stream, between gpt2_backward and
+ * gpt2_adamw_step; the norm before clipping goes to *d_norm (one device float) when d_norm is not
+ * NULL. The norm is reduced in a fixed order (bitwise reproducible). GPT2_E_INVALID unless
+ * max_norm is positive and finite. */
+gpt2_status gpt2_clip_grad_norm(gpt2_ctx* ctx, float max_norm, float* d_norm);
+
 /* AdamW ([OBJ], [MEM]): t += 1, then per element
  *   m = b1 m + (1-b1) g;  v = b2 v + (1-b2) g^2;
  *   p -= lr * ( (m / (1-b1^t)) / (sqrt(v / (1-b2^t)) + eps) + wd * p ),

@@ -430,6 +430,30 @@ def loss_and_grad(params: np.ndarray, x: np.ndarray, y: np.ndarray, cfg: Config,
     return mean_loss(rows, y), rows, grad
 
 
+def clip_grad_norm(g: np.ndarray, max_norm: float):
+    """Global-norm clipping of a flat gradient: norm = sqrt(sum g^2); the gradient times
+    max_norm / (norm + 1e-6) when that factor is below 1, else unchanged. Returns (norm, g').
+    The pages set no clipping; a training loop may ask for it."""
+    g = np.asarray(g, dtype=np.float64)
+    norm = math.sqrt(float(np.dot(g, g)))
+    coef = max_norm / (norm + 1e-6)
+    return norm, (g * coef if coef < 1.0 else g.copy())
+
+
+def cosine_lr(step: int, total_steps: int, max_lr: float, warmup_steps: int = 0,
+              min_lr: float = 0.0) -> float:
+    """Learning rate of optimiser step ``step`` (0-based) under a cosine schedule sized to the run:
+    linear warm-up over warmup_steps, then max_lr -> min_lr along half a cosine that ends at
+    total_steps ("Pré-treinar um LLM", paragraph on Chinchilla's method and learning-rate
+    schedules: the cosine must reach its end at the token budget)."""
+    if step < warmup_steps:
+        return max_lr * (step + 1) / warmup_steps
+    if step >= total_steps:
+        return min_lr
+    x = (step - warmup_steps) / max(1, total_steps - warmup_steps)
+    return min_lr + 0.5 * (max_lr - min_lr) * (1.0 + math.cos(math.pi * x))
+
+
 def adamw_update(p, g, m, v, t: int, lr: float, beta1: float, beta2: float, eps: float,
                  weight_decay, decay=None):
     """One AdamW step at step number t (t = 1 on the first step). Returns new (p, m, v) in float64.

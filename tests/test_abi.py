@@ -100,6 +100,7 @@ def test_null_context_and_ops_are_rejected(lib):
     assert lib.gpt2_forward_loss(None, None, None, None) == G.GPT2_E_INVALID
     assert lib.gpt2_backward(None, 1.0, 0) == G.GPT2_E_INVALID
     assert lib.gpt2_adamw_step(None, 1e-3, 0.9, 0.95, 1e-8, 0.1) == G.GPT2_E_INVALID
+    assert lib.gpt2_clip_grad_norm(None, 1.0, None) == G.GPT2_E_INVALID
     assert lib.gpt2_check(None) == G.GPT2_E_INVALID
     assert lib.gpt2_destroy(None) == G.GPT2_E_INVALID
     assert lib.gpt2_op_gemm(1, 1, 1, 8, 8, 8, None, 8, None, 8, None, 8, 1.0, 0.0, None) == G.GPT2_E_INVALID

@@ -228,6 +228,7 @@ struct Bufs {
   float* splitk = nullptr;
   uint32_t* keys = nullptr;
   float* segpart = nullptr;
+  float* clip = nullptr;  // gradient-norm block sums, the norm and the clipping factor
 };
 
 struct Carver {
@@ -307,6 +308,7 @@ size_t carve(const Geo& g, uintptr_t base, Bufs& b) {
   b.splitk = c.take<float>(4 * std::max<size_t>(sk, 1));
   b.keys = c.take<uint32_t>(4 * M);
   b.segpart = c.take<float>(4 * (size_t)embed_bwd_chunks(g.M) * 2 * d);
+  b.clip = c.take<float>(4 * (size_t)(CLIP_PARTS + 4));
   return (c.off + 255) & ~(size_t)255;
 }
 
@@ -764,6 +766,15 @@ gpt2_status gpt2_adamw_step(gpt2_ctx* c, float lr, float beta1, float beta2, flo
     }
     HIPCHK(hipEventRecord(c->ev_adam[r], c->side));
   }
+  return GPT2_OK;
+}
+
+gpt2_status gpt2_clip_grad_norm(gpt2_ctx* c, float max_norm, float* d_norm) {
+  STEP(check_ctx(c));
+  if (!(max_norm > 0.0f) || !isfinite(max_norm))
+    return fail(GPT2_E_INVALID, "max_norm must be positive and finite");
+  // the gradients are final on the main stream (the backward joined its side stream)
+  HIPCHK(launch_clip_grad_norm(c->g.N, c->b.grads, max_norm, c->b.clip, d_norm, c->stream));
   return GPT2_OK;
 }
 

@@ -129,6 +129,12 @@ struct AdamSeg {
 hipError_t launch_adamw(int64_t begin, int64_t n, float* p, const float* g, float* m, float* v,
                         void* shadow, const AdamSeg* segs, int nseg, float lr, float b1, float b2,
                         float eps, float wd, float bc1, float bc2, hipStream_t s);
+// Global-norm clipping of the flat gradient g (n a multiple of 4): norm = ||g||_2,
+// g *= min(1, max_norm / (norm + 1e-6)). scratch holds CLIP_PARTS + 2 floats (block sums, then
+// the norm and the factor); the norm also goes to user_norm when it is not null.
+constexpr int CLIP_PARTS = 1024;
+hipError_t launch_clip_grad_norm(int64_t n, float* g, float max_norm, float* scratch,
+                                 float* user_norm, hipStream_t s);
 hipError_t launch_init_normal(int64_t begin, int64_t count, float* p, uint64_t seed, float std,
                               hipStream_t s);
 hipError_t launch_fill(int64_t count, float* p, float value, hipStream_t s);

@@ -140,7 +140,69 @@ unsigned grid_for(int64_t work) {
   return (unsigned)(g < 1 ? 1 : (g > 8192 ? 8192 : g));
 }
 
+// Global-norm gradient clipping: ||g|| over the whole flat gradient, then g *= max / (||g|| +
+// 1e-6) when that factor is below 1. Block b of the first pass sums the squares of a fixed strided
+// set of float4s (fp32 per lane, then a fixed-order tree); the second pass adds the block sums in
+// double in a fixed order, so the norm does not depend on scheduling.
+__global__ __launch_bounds__(THREADS) void sumsq_partial_kernel(int64_t n4, const float* __restrict__ g,
+                                                                float* __restrict__ part) {
+  __shared__ float sh[THREADS / 64];
+  float s = 0.0f;
+  for (int64_t i = (int64_t)blockIdx.x * THREADS + threadIdx.x; i < n4;
+       i += (int64_t)gridDim.x * THREADS) {
+    const f32x4 v = *reinterpret_cast<const f32x4*>(g + 4 * i);
+    s = fmaf(v[0], v[0], s);
+    s = fmaf(v[1], v[1], s);
+    s = fmaf(v[2], v[2], s);
+    s = fmaf(v[3], v[3], s);
+  }
+  s = wave_sum(s);
+  if ((threadIdx.x & 63) == 0) sh[threadIdx.x >> 6] = s;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    float t = sh[0];
+    for (int w = 1; w < THREADS / 64; ++w) t += sh[w];
+    part[blockIdx.x] = t;
+  }
+}
+
+__global__ __launch_bounds__(64) void clip_coef_kernel(int nparts, const float* __restrict__ part,
+                                                       float max_norm, float* __restrict__ out,
+                                                       float* __restrict__ user_norm) {
+  if (threadIdx.x != 0) return;
+  double s = 0.0;
+  for (int i = 0; i < nparts; ++i) s += (double)part[i];
+  const float norm = (float)sqrt(s);
+  const float coef = max_norm / (norm + 1e-6f);
+  out[0] = norm;
+  out[1] = coef < 1.0f ? coef : 1.0f;
+  if (user_norm) user_norm[0] = norm;
+}
+
+__global__ __launch_bounds__(THREADS) void scale_by_kernel(int64_t n4, float* __restrict__ g,
+                                                           const float* __restrict__ coef) {
+  const float c = *coef;
+  if (c >= 1.0f) return;
+  for (int64_t i = (int64_t)blockIdx.x * THREADS + threadIdx.x; i < n4;
+       i += (int64_t)gridDim.x * THREADS) {
+    f32x4 v = *reinterpret_cast<const f32x4*>(g + 4 * i);
+    *reinterpret_cast<f32x4*>(g + 4 * i) = v * c;
+  }
+}
+
 }  // namespace
+
+hipError_t launch_clip_grad_norm(int64_t n, float* g, float max_norm, float* scratch,
+                                 float* user_norm, hipStream_t s) {
+  if (n % 4) return hipErrorInvalidValue;
+  const int64_t n4 = n / 4;
+  hipLaunchKernelGGL(sumsq_partial_kernel, dim3(CLIP_PARTS), dim3(THREADS), 0, s, n4, g, scratch);
+  hipLaunchKernelGGL(clip_coef_kernel, dim3(1), dim3(64), 0, s, CLIP_PARTS, scratch, max_norm,
+                     scratch + CLIP_PARTS, user_norm);
+  hipLaunchKernelGGL(scale_by_kernel, dim3(grid_for(n4)), dim3(THREADS), 0, s, n4, g,
+                     scratch + CLIP_PARTS + 1);
+  return hipGetLastError();
+}
 
 hipError_t launch_adamw(int64_t begin, int64_t n, float* p, const float* g, float* m, float* v,
                         void* shadow, const AdamSeg* segs, int nseg, float lr, float b1, float b2,

@@ -70,6 +70,7 @@ def load_library(path: str | None = None):
         "gpt2_forward_loss": (st, [c_void_p, c_void_p, c_void_p, c_void_p]),
         "gpt2_backward": (st, [c_void_p, c_float, c_int32]),
         "gpt2_adamw_step": (st, [c_void_p, c_float, c_float, c_float, c_float, c_float]),
+        "gpt2_clip_grad_norm": (st, [c_void_p, c_float, c_void_p]),
         "gpt2_check": (st, [c_void_p]),
         "gpt2_destroy": (st, [c_void_p]),
         "gpt2_copy_params": (st, [c_void_p, c_int32, c_void_p, c_size_t]),
@@ -152,6 +153,11 @@ class GPT2:
 
     def adamw_step(self, lr=6e-4, beta1=0.9, beta2=0.95, eps=1e-8, weight_decay=0.1):
         _check(self.lib.gpt2_adamw_step(self.ctx, lr, beta1, beta2, eps, weight_decay))
+
+    def clip_grad_norm(self, max_norm: float, norm=None):
+        """Clip the gradients to global norm max_norm; the norm before clipping goes to the
+        device float tensor ``norm`` when given."""
+        _check(self.lib.gpt2_clip_grad_norm(self.ctx, max_norm, _ptr(norm)))
 
     def check(self):
         _check(self.lib.gpt2_check(self.ctx))
