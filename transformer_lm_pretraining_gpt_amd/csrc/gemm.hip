@@ -368,6 +368,88 @@ DEV void epilogue_bf16(const f32x16 (&acc)[MB][NB], const GemmParams& p, char* b
   }
 }
 
+// GELU-backward epilogue for 64-column wave tiles: out = acc * GELU'(u), bf16, with u the saved
+// pre-activation (bf16, laid out like the output). Each 32-row block goes through the wave's LDS
+// block: the lanes load u one 16-byte row chunk each, the arithmetic runs in the MFMA register
+// layout on u read back from LDS, the bf16 results overwrite u in place and leave as 16-byte row
+// chunks. The column sums of the rounded results (the fc-bias gradient, summed from the same
+// bf16 values the weight-gradient products read) are taken from those row chunks: one partial
+// row per wave tile.
+template <int MB, int NB>
+DEV void epilogue_gelu_bwd_bf16(const f32x16 (&acc)[MB][NB], const GemmParams& p, char* buf,
+                                int row0, int col0, int lane) {
+  static_assert(NB == 2, "64-column wave tiles");
+  const int h = lane >> 5, l32 = lane & 31;
+  const int rq = lane / 8, pos = lane % 8;  // row (within 8) and 16-byte chunk of the row passes
+  // the rows of a lane's passes share one swizzle, so its chunk holds the same 8 columns in each
+  const int chunk = pos ^ epi16_swz(rq);
+  const int col8 = col0 + chunk * 8;
+  const bf16* aux = static_cast<const bf16*>(p.aux);
+  bf16* dst = static_cast<bf16*>(p.C);
+  float cs[8] = {0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+  for (int i = 0; i < MB; ++i) {
+    u32x4 un[4];
+#pragma unroll
+    for (int pass = 0; pass < 4; ++pass) {
+      const int row = row0 + i * 32 + pass * 8 + rq, col = col0 + pos * 8;
+      un[pass] = (row < p.M && col < p.N) ? ld16(aux + (int64_t)row * p.ldc + col)
+                                          : u32x4{0, 0, 0, 0};
+    }
+#pragma unroll
+    for (int pass = 0; pass < 4; ++pass)
+      *reinterpret_cast<u32x4*>(buf + epi16_off(pass * 8 + rq, pos * 8)) = un[pass];
+    __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0): this block's u is in LDS
+    asm volatile("" ::: "memory");
+#pragma unroll
+    for (int j = 0; j < NB; ++j)
+#pragma unroll
+      for (int r = 0; r < 16; r += 2) {
+        const int rr = mfma_row(r, h), col = j * 32 + l32;  // rows rr and rr + 1
+        uint16_t* a = reinterpret_cast<uint16_t*>(buf + epi16_off(rr, col));
+        uint16_t* b = reinterpret_cast<uint16_t*>(buf + epi16_off(rr + 1, col));
+        const float x0 = acc[i][j][r] * gelu_grad_fast(bf16lo(*a));
+        const float x1 = acc[i][j][r + 1] * gelu_grad_fast(bf16lo(*b));
+        const uint32_t pk = pack_bf16(x0, x1);
+        *a = (uint16_t)pk;
+        *b = (uint16_t)(pk >> 16);
+      }
+    __builtin_amdgcn_s_waitcnt(0xc07f);
+    asm volatile("" ::: "memory");
+#pragma unroll
+    for (int pass = 0; pass < 4; ++pass) {
+      const int rl = pass * 8 + rq;
+      const u32x4 v = *reinterpret_cast<const u32x4*>(buf + rl * 128 + pos * 16);
+      const int row = row0 + i * 32 + rl;
+      if (row < p.M && col8 < p.N) {
+        *reinterpret_cast<u32x4*>(dst + (int64_t)row * p.ldc + col8) = v;
+#pragma unroll
+        for (int w = 0; w < 4; ++w) {
+          cs[2 * w] += bf16lo(v[w]);
+          cs[2 * w + 1] += bf16hi(v[w]);
+        }
+      }
+    }
+    __builtin_amdgcn_s_waitcnt(0xc07f);
+    asm volatile("" ::: "memory");
+  }
+  if (p.colsum) {
+    // lanes holding the same chunk: rq 0..3 at pos = chunk, rq 4..7 at pos = chunk ^ 4; add them
+    // in a fixed order, then lanes 0..7 write the wave's partial row
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      cs[e] += __shfl_xor(cs[e], 8, 64);
+      cs[e] += __shfl_xor(cs[e], 16, 64);
+      cs[e] += __shfl_xor(cs[e], 36, 64);
+    }
+    if (rq == 0 && col8 < p.N) {
+      float* prow = p.colsum + (int64_t)(row0 / (MB * 32)) * p.N + col8;
+      *reinterpret_cast<f32x4*>(prow) = f32x4{cs[0], cs[1], cs[2], cs[3]};
+      *reinterpret_cast<f32x4*>(prow + 4) = f32x4{cs[4], cs[5], cs[6], cs[7]};
+    }
+  }
+}
+
 template <int EPI, int MB, int NB>
 DEV void epilogue_rows(const f32x16 (&acc)[MB][NB], const GemmParams& p, float* buf, int row0,
                        int col0, int lane) {
@@ -379,7 +461,6 @@ DEV void epilogue_rows(const f32x16 (&acc)[MB][NB], const GemmParams& p, float* 
   const int h = lane >> 5, l32 = lane & 31;
   float* cf = static_cast<float*>(p.C);
   if (EPI == EPI_F32) cf += (int64_t)blockIdx.z * p.c_split_stride;
-  float csum[4] = {0.0f, 0.0f, 0.0f, 0.0f};  // EPI_GELU_BWD column sums of this lane's 4 columns
 #pragma unroll
   for (int i = 0; i < MB; ++i) {
 #pragma unroll
@@ -422,10 +503,7 @@ DEV void epilogue_rows(const f32x16 (&acc)[MB][NB], const GemmParams& p, float* 
             const u32x2 u = ld8(static_cast<const bf16*>(p.aux) + o);
             const float uf[4] = {bf16lo(u[0]), bf16hi(u[0]), bf16lo(u[1]), bf16hi(u[1])};
 #pragma unroll
-            for (int e = 0; e < 4; ++e) {
-              out[e] = v[e] * gelu_grad_fast(uf[e]);
-              csum[e] += out[e];
-            }
+            for (int e = 0; e < 4; ++e) out[e] = v[e] * gelu_grad_fast(uf[e]);
             st8(static_cast<bf16*>(p.C) + o, u32x2{pack_bf16(out[0], out[1]), pack_bf16(out[2], out[3])});
           } else {
             f32x4 prev = f32x4{0, 0, 0, 0};
@@ -436,21 +514,6 @@ DEV void epilogue_rows(const f32x16 (&acc)[MB][NB], const GemmParams& p, float* 
       }
       __builtin_amdgcn_s_waitcnt(0xc07f);
       asm volatile("" ::: "memory");
-    }
-  }
-  if constexpr (EPI == EPI_GELU_BWD && 64 % V4 == 0) {  // not with 96-column wave tiles
-    if (p.colsum) {
-      // lanes c4, c4 + V4, ... hold the same columns: add them in a fixed order, then lanes
-      // 0 .. V4-1 write the wave's partial row for its WM-row block
-#pragma unroll
-      for (int sh = V4; sh < 64; sh <<= 1)
-#pragma unroll
-        for (int e = 0; e < 4; ++e) csum[e] += __shfl_xor(csum[e], sh, 64);
-      const int col = col0 + (lane % V4) * 4;
-      if (lane < V4 && col < p.N) {
-        float* dst = p.colsum + (int64_t)(row0 / (MB * 32)) * p.N + col;
-        *reinterpret_cast<f32x4*>(dst) = f32x4{csum[0], csum[1], csum[2], csum[3]};
-      }
     }
   }
 }
@@ -759,7 +822,10 @@ __global__ __launch_bounds__(64 * NW, MINB) void gemm_dma_kernel(GemmParams p) {
         else epilogue_rows<EPI_BIAS_GELU, MB, NB>(acc, p, buf, row0, col0, lane);
         break;
       case EPI_BIAS_RESID: epilogue_rows<EPI_BIAS_RESID, MB, NB>(acc, p, buf, row0, col0, lane); break;
-      case EPI_GELU_BWD: epilogue_rows<EPI_GELU_BWD, MB, NB>(acc, p, buf, row0, col0, lane); break;
+      case EPI_GELU_BWD:
+        if constexpr (NB == 2) epilogue_gelu_bwd_bf16<MB, NB>(acc, p, buf16, row0, col0, lane);
+        else epilogue_rows<EPI_GELU_BWD, MB, NB>(acc, p, buf, row0, col0, lane);
+        break;
       default: epilogue_rows<EPI_F32, MB, NB>(acc, p, buf, row0, col0, lane); break;
     }
     if (wnext >= w_end) break;

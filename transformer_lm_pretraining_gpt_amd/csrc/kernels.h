@@ -32,8 +32,8 @@ struct GemmParams {
   // when set, alpha is multiplied by this device scalar (read once per block): the loss scale
   // 1 / (number of trained positions) that only the device knows
   const float* alpha_scale;
-  // EPI_GELU_BWD on the direct-to-LDS path only: when set, column sums of the output over each
-  // 128-row block of a wave tile go to colsum[(row / 128) * N + col] (fp32, before rounding)
+  // EPI_GELU_BWD on the direct-to-LDS path with 64-column wave tiles only: when set, column sums
+  // of the bf16 output over each 128-row block of a wave tile go to colsum[(row / 128) * N + col]
   float* colsum;
 };
 
