@@ -368,6 +368,55 @@ DEV void epilogue_bf16(const f32x16 (&acc)[MB][NB], const GemmParams& p, char* b
   }
 }
 
+// bf16 store (alpha, bias) for 96-column wave tiles: as epilogue_bf16, in 16-row halves of each
+// 32-row block (16 x 96 bf16 fit the wave's LDS block). Rows are 208 bytes apart (192 + 16), so
+// the two lane halves, which write rows four apart, fall on disjoint banks; each lane then reads
+// 16-byte row chunks (three passes over the 12 chunks of 16 rows) and stores them.
+constexpr int EPI96_PITCH = 208;
+template <int MB, int NB>
+DEV void epilogue_bf16_96(const f32x16 (&acc)[MB][NB], const GemmParams& p, char* buf, int row0,
+                          int col0, int lane) {
+  static_assert(NB == 3, "96-column wave tiles");
+  static_assert(16 * EPI96_PITCH <= 4096, "the wave's LDS block");
+  const int h = lane >> 5, l32 = lane & 31;
+  float bias[NB];
+#pragma unroll
+  for (int j = 0; j < NB; ++j) {
+    const int col = col0 + j * 32 + l32;
+    bias[j] = (p.bias && col < p.N) ? p.bias[col] : 0.0f;
+  }
+  bf16* dst = static_cast<bf16*>(p.C);
+#pragma unroll
+  for (int i = 0; i < MB; ++i) {
+#pragma unroll
+    for (int half = 0; half < 2; ++half) {
+#pragma unroll
+      for (int j = 0; j < NB; ++j)
+#pragma unroll
+        for (int r = 8 * half; r < 8 * half + 8; r += 2) {
+          const float x0 = p.alpha * acc[i][j][r] + bias[j];
+          const float x1 = p.alpha * acc[i][j][r + 1] + bias[j];
+          const uint32_t pk = pack_bf16(x0, x1);
+          const int rr = mfma_row(r, h) - 16 * half, col = j * 32 + l32;  // rows rr and rr + 1
+          *reinterpret_cast<uint16_t*>(buf + rr * EPI96_PITCH + col * 2) = (uint16_t)pk;
+          *reinterpret_cast<uint16_t*>(buf + (rr + 1) * EPI96_PITCH + col * 2) = (uint16_t)(pk >> 16);
+        }
+      __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0): this wave's LDS writes are done
+      asm volatile("" ::: "memory");
+#pragma unroll
+      for (int pass = 0; pass < 3; ++pass) {
+        const int idx = pass * 64 + lane;
+        const int rl = idx / 12, ch = idx % 12;
+        const u32x4 v = *reinterpret_cast<const u32x4*>(buf + rl * EPI96_PITCH + ch * 16);
+        const int row = row0 + i * 32 + 16 * half + rl, col = col0 + ch * 8;
+        if (row < p.M && col < p.N) *reinterpret_cast<u32x4*>(dst + (int64_t)row * p.ldc + col) = v;
+      }
+      __builtin_amdgcn_s_waitcnt(0xc07f);
+      asm volatile("" ::: "memory");
+    }
+  }
+}
+
 // GELU-backward epilogue for 64-column wave tiles: out = acc * GELU'(u), bf16, with u the saved
 // pre-activation (bf16, laid out like the output). Each 32-row block goes through the wave's LDS
 // block: the lanes load u one 16-byte row chunk each, the arithmetic runs in the MFMA register
@@ -815,6 +864,7 @@ __global__ __launch_bounds__(64 * NW, MINB) void gemm_dma_kernel(GemmParams p) {
     switch (p.epi) {
       case EPI_STORE:
         if constexpr (NB == 2) epilogue_bf16<EPI_STORE, MB, NB, TAG == 1>(acc, p, buf16, row0, col0, lane);
+        else if constexpr (NB == 3) epilogue_bf16_96<MB, NB>(acc, p, buf16, row0, col0, lane);
         else epilogue_rows<EPI_STORE, MB, NB>(acc, p, buf, row0, col0, lane);
         break;
       case EPI_BIAS_GELU:
