@@ -189,7 +189,9 @@ ColLayout col_layout(const Geo& g) {
   cl.nparts_ln = ln_bwd_blocks(g.M, LN_ROWS_PER_BLOCK);
   cl.nparts_qkv = (g.M + COLSUM_ROWS_PER_BLOCK - 1) / COLSUM_ROWS_PER_BLOCK;
   if (fused_colsum(g)) {
-    const int bm = pick_tile(g, g.M, 4 * g.d) == TILE_256 ? 256 : 128;
+    // rows per block of the product that writes the partial rows (128 x 384 tiles fall back to
+    // 256 x 256 when column sums are asked for)
+    const int bm = pick_tile(g, g.M, 4 * g.d) == TILE_128 ? 128 : 256;
     cl.nparts_fc = 2 * ((g.M + bm - 1) / bm);
   } else {
     cl.nparts_fc = cl.nparts_qkv;

@@ -1028,9 +1028,15 @@ int gemm_k_tile(bool is_bf16) { return is_bf16 ? ROWB / 2 : ROWB / 4; }
 
 int gemm_pick_tile(int M, int N) {
   const int64_t t256 = (int64_t)((M + 255) / 256) * ((N + 255) / 256);
-  // An output of 192 .. 255 tiles of 256 x 256 leaves CUs idle for the whole product; where N is
-  // a multiple of 384 the 128 x 384 tile (same block shape, 8 waves) splits it into 4/3 as many.
-  if (t256 >= 192 && t256 < 256 && N % 384 == 0) return TILE_128x384;
+  // Both large tiles run one 8-wave block per CU, a round of tiles per 256 CUs. Where N is a
+  // multiple of 384, the 128 x 384 tile (3/4 of the work of a 256 x 256 one) is taken when its
+  // rounds cost at least 10 % less: a partly filled last round of 256 x 256 tiles leaves CUs idle
+  // (an output of 192 tiles, or the QKV product's 2.25 rounds).
+  if (N % 384 == 0) {
+    const int64_t t384 = (int64_t)((M + 127) / 128) * (N / 384);
+    const int64_t c256 = 4 * ((t256 + 255) / 256), c384 = 3 * ((t384 + 255) / 256);
+    if (c384 < c256 && 10 * (c256 - c384) >= c256) return TILE_128x384;
+  }
   return t256 >= 192 ? TILE_256 : TILE_128;
 }
 
