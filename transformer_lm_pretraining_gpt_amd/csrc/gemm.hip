@@ -417,6 +417,59 @@ DEV void epilogue_bf16_96(const f32x16 (&acc)[MB][NB], const GemmParams& p, char
   }
 }
 
+// Bias + residual, fp32 out, for 96-column wave tiles: 8 rows at a time go through the wave's
+// fp32 LDS block and come back as 8 x 24 float4, three full passes of the 64 lanes. The residual
+// float4s of the 8 rows are requested before the block's stores (one memory round trip per 8
+// rows, not one per pass) and each lane's three bias float4s are read once.
+template <int MB, int NB>
+DEV void epilogue_resid_96(const f32x16 (&acc)[MB][NB], const GemmParams& p, float* buf,
+                           int row0, int col0, int lane) {
+  static_assert(NB == 3, "96-column wave tiles");
+  constexpr int PITCH = epi_pitch<NB>();
+  const int h = lane >> 5, l32 = lane & 31;
+  float* cf = static_cast<float*>(p.C);
+  int rl[3], c4[3];
+  f32x4 bias[3];
+#pragma unroll
+  for (int pass = 0; pass < 3; ++pass) {
+    const int idx = pass * 64 + lane;
+    rl[pass] = idx / 24;
+    c4[pass] = idx % 24;
+    const int col = col0 + 4 * c4[pass];
+    bias[pass] = (p.bias && col < p.N) ? *reinterpret_cast<const f32x4*>(p.bias + col)
+                                       : f32x4{0, 0, 0, 0};
+  }
+#pragma unroll
+  for (int i = 0; i < MB; ++i) {
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      f32x4 rs[3];
+#pragma unroll
+      for (int pass = 0; pass < 3; ++pass) {
+        const int row = row0 + i * 32 + 8 * q + rl[pass], col = col0 + 4 * c4[pass];
+        rs[pass] = (row < p.M && col < p.N)
+                       ? *reinterpret_cast<const f32x4*>(p.resid + (int64_t)row * p.ldc + col)
+                       : f32x4{0, 0, 0, 0};
+      }
+#pragma unroll
+      for (int j = 0; j < NB; ++j)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) buf[(4 * h + e) * PITCH + j * 32 + l32] = acc[i][j][4 * q + e];
+      __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0): this wave's LDS writes are done
+      asm volatile("" ::: "memory");
+#pragma unroll
+      for (int pass = 0; pass < 3; ++pass) {
+        const f32x4 v = *reinterpret_cast<const f32x4*>(buf + rl[pass] * PITCH + 4 * c4[pass]);
+        const int row = row0 + i * 32 + 8 * q + rl[pass], col = col0 + 4 * c4[pass];
+        if (row < p.M && col < p.N)
+          *reinterpret_cast<f32x4*>(cf + (int64_t)row * p.ldc + col) = rs[pass] + v + bias[pass];
+      }
+      __builtin_amdgcn_s_waitcnt(0xc07f);
+      asm volatile("" ::: "memory");
+    }
+  }
+}
+
 // GELU-backward epilogue for 64-column wave tiles: out = acc * GELU'(u), bf16, with u the saved
 // pre-activation (bf16, laid out like the output). Each 32-row block goes through the wave's LDS
 // block: the lanes load u one 16-byte row chunk each, the arithmetic runs in the MFMA register
@@ -871,7 +924,10 @@ __global__ __launch_bounds__(64 * NW, MINB) void gemm_dma_kernel(GemmParams p) {
         if constexpr (NB == 2) epilogue_bf16<EPI_BIAS_GELU, MB, NB, false>(acc, p, buf16, row0, col0, lane);
         else epilogue_rows<EPI_BIAS_GELU, MB, NB>(acc, p, buf, row0, col0, lane);
         break;
-      case EPI_BIAS_RESID: epilogue_rows<EPI_BIAS_RESID, MB, NB>(acc, p, buf, row0, col0, lane); break;
+      case EPI_BIAS_RESID:
+        if constexpr (NB == 3) epilogue_resid_96<MB, NB>(acc, p, buf, row0, col0, lane);
+        else epilogue_rows<EPI_BIAS_RESID, MB, NB>(acc, p, buf, row0, col0, lane);
+        break;
       case EPI_GELU_BWD:
         if constexpr (NB == 2) epilogue_gelu_bwd_bf16<MB, NB>(acc, p, buf16, row0, col0, lane);
         else epilogue_rows<EPI_GELU_BWD, MB, NB>(acc, p, buf, row0, col0, lane);
