@@ -363,7 +363,7 @@ struct gpt2_ctx {
   hipStream_t stream;
   // side stream for work off the forward's critical path (the token sort), joined by events
   hipStream_t side = nullptr;
-  hipEvent_t fork = nullptr, join = nullptr;
+  hipEvent_t fork = nullptr, join = nullptr, tail = nullptr;
   // backward: LayerNorm slot k done (2L + 1), dbig and dqkv of layer l written (L each)
   std::vector<hipEvent_t> ev_ln, ev_dbig, ev_dqkv;
   // AdamW: parameter range r updated (embeddings, layers 0 .. L-1, final LayerNorm: L + 2)
@@ -603,10 +603,15 @@ gpt2_status backward(gpt2_ctx* c, float grad_scale, int acc) {
   }
   HIPCHK(hipEventRecord(c->join, side));
   HIPCHK(hipStreamWaitEvent(c->stream, c->join, 0));
+  // Every bias and LayerNorm gain/shift gradient from its partial rows, in one launch on the side
+  // stream once the last LayerNorm backward has written its rows, beside the embedding backward;
+  // the main stream waits for it before the backward ends.
+  HIPCHK(hipStreamWaitEvent(side, c->ev_ln[0], 0));
+  HIPCHK(launch_colsum_reduce_batch(b.coltasks, b.ncoltasks, b.ncolblocks, acc, side));
+  HIPCHK(hipEventRecord(c->tail, side));
   HIPCHK(launch_embed_bwd(g.B, g.T, d, b.keys, b.dres, G + g.wte, G + g.wpe, acc, b.segpart,
                           c->stream));
-  // every bias and LayerNorm gain/shift gradient from its partial rows, in one launch
-  HIPCHK(launch_colsum_reduce_batch(b.coltasks, b.ncoltasks, b.ncolblocks, acc, c->stream));
+  HIPCHK(hipStreamWaitEvent(c->stream, c->tail, 0));
   return GPT2_OK;
 }
 
@@ -663,6 +668,7 @@ gpt2_status gpt2_init(const gpt2_config* cfg, void* d_arena, size_t arena_bytes,
   auto bail = [&](gpt2_status s) {
     if (c->fork) hipEventDestroy(c->fork);
     if (c->join) hipEventDestroy(c->join);
+    if (c->tail) hipEventDestroy(c->tail);
     for (auto* v : {&c->ev_ln, &c->ev_dbig, &c->ev_dqkv, &c->ev_adam})
       for (hipEvent_t e : *v)
         if (e) hipEventDestroy(e);
@@ -699,6 +705,7 @@ gpt2_status gpt2_init(const gpt2_config* cfg, void* d_arena, size_t arena_bytes,
   INITCHK(hipStreamCreateWithFlags(&c->side, hipStreamNonBlocking));
   INITCHK(hipEventCreateWithFlags(&c->fork, hipEventDisableTiming));
   INITCHK(hipEventCreateWithFlags(&c->join, hipEventDisableTiming));
+  INITCHK(hipEventCreateWithFlags(&c->tail, hipEventDisableTiming));
   c->ev_ln.assign(2 * g.L + 1, nullptr);
   c->ev_dbig.assign(g.L, nullptr);
   c->ev_dqkv.assign(g.L, nullptr);
@@ -801,6 +808,7 @@ gpt2_status gpt2_destroy(gpt2_ctx* c) {
   for (hipEvent_t e : c->ev) hipEventDestroy(e);
   if (c->fork) hipEventDestroy(c->fork);
   if (c->join) hipEventDestroy(c->join);
+  if (c->tail) hipEventDestroy(c->tail);
   for (auto* v : {&c->ev_ln, &c->ev_dbig, &c->ev_dqkv, &c->ev_adam})
     for (hipEvent_t e : *v)
       if (e) hipEventDestroy(e);
