@@ -918,28 +918,18 @@ __global__ __launch_bounds__(THREADS, 2) void attn_bwd_dq64_kernel(
           for (int db = 0; db < 2; ++db)
             Mfma<bf16>::mma(dq[i][db], HeadTile::tfrag(ktile, db * 32, js * 32 + 16 * u, lane), dsb[u]);
       };
-      if (key0 + 63 <= qg[i]) {
-        // every key of the tile is at or before every query of the group (no mask): both
-        // sub-tiles as one straight-line block
-        f32x16 s0, d0, s1, d1;
-        u32x4 ds0[2], ds1[2];
-        scores(0, s0, d0);
-        scores(1, s1, d1);
-        dscores(0, false, s0, d0, ds0);
-        accumulate(0, ds0);
-        dscores(1, false, s1, d1, ds1);
-        accumulate(1, ds1);
-      } else {
+      // The two 32-key sub-tiles one after the other: keeping both sub-tiles' scores live (so
+      // one's MFMAs overlap the other's exponentials) needs more registers than the 256 a wave
+      // has at two blocks per CU, and the spill reloads' vmcnt waits drained the K/V prefetch.
 #pragma unroll
-        for (int js = 0; js < 2; ++js) {
-          const int j0 = key0 + js * 32;
-          if (j0 > qg[i] + 31) continue;
-          f32x16 sacc, dpacc;
-          u32x4 dsb[2];
-          scores(js, sacc, dpacc);
-          dscores(js, j0 + 31 > qg[i], sacc, dpacc, dsb);
-          accumulate(js, dsb);
-        }
+      for (int js = 0; js < 2; ++js) {
+        const int j0 = key0 + js * 32;
+        if (j0 > qg[i] + 31) continue;
+        f32x16 sacc, dpacc;
+        u32x4 dsb[2];
+        scores(js, sacc, dpacc);
+        dscores(js, j0 + 31 > qg[i], sacc, dpacc, dsb);
+        accumulate(js, dsb);
       }
     }
     };
