@@ -151,16 +151,20 @@ int pick_tile(const Geo& g, int M, int N) {
 }
 
 // Split of the K = rows reduction of a weight gradient (in x out, K = tokens); the fp32 partials
-// are summed by a second kernel in a fixed order. bf16 runs 256x256 tiles at one block per CU, so
-// the splits aim at one round of about 256 blocks (measured best on the GPT-2 shapes); fp32 runs
-// 128x128 tiles and aims at about 1024 blocks.
+// are summed by a second kernel in a fixed order. bf16 runs 256x256 tiles at one block per CU and
+// the splits aim at about 160 blocks, fewer than the 256 CUs: these products run on the side
+// stream, and the CUs they leave free take the main stream's LayerNorm, attention and
+// input-gradient kernels, which otherwise wait for whole products to drain (step time measured
+// with targets 256, 224, 192, 160, 128, 96 and 64 blocks: 160 best, 1.5% below 256; 96 and
+// fewer leave the weight gradients on the critical path). fp32 runs 128x128 tiles and aims at
+// about 1024 blocks.
 struct Split { int splits, k_split; };
 Split pick_split(const Geo& g, int in, int out) {
   const int kt = 64;
   int s;
   if (g.bf16) {
     const int64_t tiles = (int64_t)((in + 255) / 256) * ((out + 255) / 256);
-    s = (int)(256 / tiles);
+    s = (int)(160 / tiles);
     if (s > 16) s = 16;
   } else {
     const int64_t tiles = (int64_t)((in + 127) / 128) * ((out + 127) / 128);
