@@ -212,7 +212,6 @@ ColLayout col_layout(const Geo& g) {
 struct Bufs {
   float *params = nullptr, *grads = nullptr, *m = nullptr, *v = nullptr;
   void* shadow = nullptr;
-  AdamSeg* segs = nullptr;
   std::vector<float*> resid, resid_mid, ln1_mean, ln1_rstd, ln2_mean, ln2_rstd, lse;
   std::vector<void*> ln1, qkv, att, ln2, fc, act;
   void* lnf = nullptr;
@@ -258,7 +257,6 @@ size_t carve(const Geo& g, uintptr_t base, Bufs& b) {
   b.m = c.take<float>(4 * N);
   b.v = c.take<float>(4 * N);
   b.shadow = g.bf16 ? c.take<void>(2 * N) : nullptr;
-  b.segs = c.take<AdamSeg>(sizeof(AdamSeg) * decay_segments(g).size());
   const size_t bht = (size_t)g.B * g.H * g.T;
   b.resid.resize(g.L + 1);
   b.resid_mid.resize(g.L);
@@ -699,8 +697,6 @@ gpt2_status gpt2_init(const gpt2_config* cfg, void* d_arena, size_t arena_bytes,
   if (g.bf16) INITCHK(launch_cast_bf16(g.N, b.params, b.shadow, c->stream));
   INITCHK(hipMemsetAsync(b.err, 0, sizeof(int), c->stream));
   INITCHK(hipMemsetAsync(b.loss, 0, 2 * sizeof(float), c->stream));
-  INITCHK(hipMemcpyAsync(b.segs, c->segs.data(), sizeof(AdamSeg) * c->segs.size(),
-                         hipMemcpyHostToDevice, c->stream));
   const std::vector<ColTask> coltasks = col_tasks(g, b);
   b.ncoltasks = (int)coltasks.size();
   b.ncolblocks = coltasks.empty() ? 0 : coltasks.back().block0 + (coltasks.back().n + 63) / 64;
@@ -761,9 +757,9 @@ gpt2_status gpt2_adamw_step(gpt2_ctx* c, float lr, float beta1, float beta2, flo
   for (int64_t x : cut) aligned = aligned && x % 4 == 0;
   if (!aligned) {
     Timed t(c, FAM_ADAMW, 30.0 * g.N);
-    HIPCHK(launch_adamw(0, g.N, c->b.params, c->b.grads, c->b.m, c->b.v, c->b.shadow, c->b.segs,
-                        (int)c->segs.size(), lr, beta1, beta2, eps, weight_decay, (float)bc1,
-                        (float)bc2, c->stream));
+    HIPCHK(launch_adamw(0, g.N, c->b.params, c->b.grads, c->b.m, c->b.v, c->b.shadow,
+                        c->segs.data(), (int)c->segs.size(), lr, beta1, beta2, eps, weight_decay,
+                        (float)bc1, (float)bc2, c->stream));
     for (hipEvent_t e : c->ev_adam) HIPCHK(hipEventRecord(e, c->stream));
     return GPT2_OK;
   }
@@ -774,7 +770,7 @@ gpt2_status gpt2_adamw_step(gpt2_ctx* c, float lr, float beta1, float beta2, flo
     {
       Timed t(c, FAM_ADAMW, 30.0 * n, c->side);
       HIPCHK(launch_adamw(cut[r], n, c->b.params, c->b.grads, c->b.m, c->b.v, c->b.shadow,
-                          c->b.segs, (int)c->segs.size(), lr, beta1, beta2, eps, weight_decay,
+                          c->segs.data(), (int)c->segs.size(), lr, beta1, beta2, eps, weight_decay,
                           (float)bc1, (float)bc2, c->side));
     }
     HIPCHK(hipEventRecord(c->ev_adam[r], c->side));

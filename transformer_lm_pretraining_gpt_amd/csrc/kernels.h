@@ -125,7 +125,9 @@ struct AdamSeg {
   int decay;
   int pad;
 };
-// AdamW over elements [begin, begin + n) of the flat arrays (begin and n multiples of 4).
+// AdamW over elements [begin, begin + n) of the flat arrays (begin and n multiples of 4). segs is a
+// host array (sorted, the first run beginning at 0, every begin a multiple of 4); the launcher
+// passes the runs that meet the range to the kernel by value.
 hipError_t launch_adamw(int64_t begin, int64_t n, float* p, const float* g, float* m, float* v,
                         void* shadow, const AdamSeg* segs, int nseg, float lr, float b1, float b2,
                         float eps, float wd, float bc1, float bc2, hipStream_t s);

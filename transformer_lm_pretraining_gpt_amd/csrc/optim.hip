@@ -21,26 +21,32 @@ namespace {
 
 constexpr int THREADS = 256;
 
+// The decay runs that meet one launch's range, by value (kernel arguments are read with scalar
+// loads, so the per-element lookup is a few compares against uniform values).
+constexpr int ADAM_RUNS = 16;
+struct AdamRuns {
+  int64_t begin[ADAM_RUNS];  // begin[0] <= first element of the launch
+  uint32_t decay;            // bit j: run j is decayed
+  int n;
+};
+
 __global__ __launch_bounds__(THREADS) void adamw_kernel(int64_t begin, int64_t n4,
                                                         float* __restrict__ p,
                                                         const float* __restrict__ g,
                                                         float* __restrict__ m,
                                                         float* __restrict__ v,
-                                                        bf16* __restrict__ shadow,
-                                                        const AdamSeg* __restrict__ segs,
-                                                        int nseg, float lr, float b1, float b2,
-                                                        float eps, float wd, float bc1,
-                                                        float bc2) {
+                                                        bf16* __restrict__ shadow, AdamRuns runs,
+                                                        float lr, float b1, float b2, float eps,
+                                                        float wd, float bc1, float bc2) {
   for (int64_t i = (int64_t)blockIdx.x * THREADS + threadIdx.x; i < n4;
        i += (int64_t)gridDim.x * THREADS) {
     const int64_t e = begin + 4 * i;
-    // segment holding element e (segments are sorted, the first begins at 0)
-    int lo = 0, hi = nseg - 1;
-    while (lo < hi) {
-      const int mid = (lo + hi + 1) >> 1;
-      if (segs[mid].begin <= e) lo = mid; else hi = mid - 1;
-    }
-    const float wdi = segs[lo].decay ? wd : 0.0f;
+    // run holding element e (its four elements share it: run boundaries are multiples of 4)
+    uint32_t dec = runs.decay & 1u;
+#pragma unroll
+    for (int j = 1; j < ADAM_RUNS; ++j)
+      if (j < runs.n && e >= runs.begin[j]) dec = (runs.decay >> j) & 1u;
+    const float wdi = dec ? wd : 0.0f;
     f32x4 pv = *reinterpret_cast<const f32x4*>(p + e);
     const f32x4 gv = *reinterpret_cast<const f32x4*>(g + e);
     f32x4 mv = *reinterpret_cast<const f32x4*>(m + e);
@@ -207,12 +213,34 @@ hipError_t launch_clip_grad_norm(int64_t n, float* g, float max_norm, float* scr
 hipError_t launch_adamw(int64_t begin, int64_t n, float* p, const float* g, float* m, float* v,
                         void* shadow, const AdamSeg* segs, int nseg, float lr, float b1, float b2,
                         float eps, float wd, float bc1, float bc2, hipStream_t s) {
-  if (n % 4 || begin % 4) return hipErrorInvalidValue;
-  const int64_t n4 = n / 4;
-  if (n4 == 0) return hipSuccess;
-  hipLaunchKernelGGL(adamw_kernel, dim3(grid_for(n4)), dim3(THREADS), 0, s, begin, n4, p, g, m, v,
-                     static_cast<bf16*>(shadow), segs, nseg, lr, b1, b2, eps, wd, bc1, bc2);
-  return hipGetLastError();
+  if (n % 4 || begin % 4 || nseg < 1 || segs[0].begin != 0) return hipErrorInvalidValue;
+  const int64_t end = begin + n;
+  // run holding `begin`, then one launch per ADAM_RUNS runs
+  int r = 0;
+  while (r + 1 < nseg && segs[r + 1].begin <= begin) ++r;
+  for (int64_t lo = begin; lo < end;) {
+    AdamRuns runs{};
+    int64_t hi = end;
+    for (int j = 0; r + j < nseg; ++j) {
+      const int64_t b = segs[r + j].begin;
+      if (j > 0 && b >= end) break;
+      if (j == ADAM_RUNS) {
+        hi = b;
+        break;
+      }
+      if (b % 4) return hipErrorInvalidValue;
+      runs.begin[j] = b;
+      runs.decay |= (segs[r + j].decay ? 1u : 0u) << j;
+      runs.n = j + 1;
+    }
+    const int64_t n4 = (hi - lo) / 4;
+    hipLaunchKernelGGL(adamw_kernel, dim3(grid_for(n4)), dim3(THREADS), 0, s, lo, n4, p, g, m, v,
+                       static_cast<bf16*>(shadow), runs, lr, b1, b2, eps, wd, bc1, bc2);
+    if (hipError_t e = hipGetLastError(); e != hipSuccess) return e;
+    r += runs.n;  // the next launch starts at the run that begins at hi
+    lo = hi;
+  }
+  return hipSuccess;
 }
 
 hipError_t launch_init_normal(int64_t begin, int64_t count, float* p, uint64_t seed, float stdv,
