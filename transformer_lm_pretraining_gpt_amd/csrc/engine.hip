@@ -366,6 +366,7 @@ struct gpt2_ctx {
   // side stream for work off the forward's critical path (the token sort), joined by events
   hipStream_t side = nullptr;
   hipEvent_t fork = nullptr, join = nullptr, tail = nullptr;
+  hipEvent_t wte_dw = nullptr;  // the LM head's (tied) weight gradient is written
   // backward: LayerNorm slot k done (2L + 1), dbig and dqkv of layer l written (L each)
   std::vector<hipEvent_t> ev_ln, ev_dbig, ev_dqkv;
   // AdamW: parameter range r updated (embeddings, layers 0 .. L-1, final LayerNorm: L + 2)
@@ -559,6 +560,7 @@ gpt2_status backward(gpt2_ctx* c, float grad_scale, int acc) {
     p.alpha_scale = inv_n;
     Timed t(c, FAM_GEMM, 2.0 * g.Vp * d * M, side);
     HIPCHK(launch_gemm(g.bf16, 0, 0, pick_tile(g, g.Vp, d), 1, 0, p, side));
+    HIPCHK(hipEventRecord(c->wte_dw, side));
   }
   const int epi_dy = g.bf16 ? EPI_STORE : EPI_F32;
   STEP(gemm(c, 1, 0, M, d, g.Vp, b.logits, g.Vp, W(c, g.wte), d, epi_dy, b.dtmp, d, nullptr,
@@ -603,14 +605,15 @@ gpt2_status backward(gpt2_ctx* c, float grad_scale, int acc) {
     STEP(ln_backward(c, b.resid[l], b.ln1_mean[l], b.ln1_rstd[l], g.ln1g(l), 1, 2 * l));
     HIPCHK(hipEventRecord(c->ev_ln[2 * l], c->stream));
   }
-  HIPCHK(hipEventRecord(c->join, side));
-  HIPCHK(hipStreamWaitEvent(c->stream, c->join, 0));
   // Every bias and LayerNorm gain/shift gradient from its partial rows, in one launch on the side
   // stream once the last LayerNorm backward has written its rows, beside the embedding backward;
-  // the main stream waits for it before the backward ends.
+  // the main stream waits for it, and so for all the side stream's work, before the backward
+  // ends. The embedding backward adds into the tied wte gradient, so it waits only for the LM
+  // head's weight gradient, not for the side stream's last weight gradients.
   HIPCHK(hipStreamWaitEvent(side, c->ev_ln[0], 0));
   HIPCHK(launch_colsum_reduce_batch(b.coltasks, b.ncoltasks, b.ncolblocks, acc, side));
   HIPCHK(hipEventRecord(c->tail, side));
+  HIPCHK(hipStreamWaitEvent(c->stream, c->wte_dw, 0));
   HIPCHK(launch_embed_bwd(g.B, g.T, d, b.keys, b.dres, G + g.wte, G + g.wpe, acc, b.segpart,
                           c->stream));
   HIPCHK(hipStreamWaitEvent(c->stream, c->tail, 0));
@@ -671,6 +674,7 @@ gpt2_status gpt2_init(const gpt2_config* cfg, void* d_arena, size_t arena_bytes,
     if (c->fork) hipEventDestroy(c->fork);
     if (c->join) hipEventDestroy(c->join);
     if (c->tail) hipEventDestroy(c->tail);
+    if (c->wte_dw) hipEventDestroy(c->wte_dw);
     for (auto* v : {&c->ev_ln, &c->ev_dbig, &c->ev_dqkv, &c->ev_adam})
       for (hipEvent_t e : *v)
         if (e) hipEventDestroy(e);
@@ -706,6 +710,7 @@ gpt2_status gpt2_init(const gpt2_config* cfg, void* d_arena, size_t arena_bytes,
   INITCHK(hipEventCreateWithFlags(&c->fork, hipEventDisableTiming));
   INITCHK(hipEventCreateWithFlags(&c->join, hipEventDisableTiming));
   INITCHK(hipEventCreateWithFlags(&c->tail, hipEventDisableTiming));
+  INITCHK(hipEventCreateWithFlags(&c->wte_dw, hipEventDisableTiming));
   c->ev_ln.assign(2 * g.L + 1, nullptr);
   c->ev_dbig.assign(g.L, nullptr);
   c->ev_dqkv.assign(g.L, nullptr);
@@ -809,6 +814,7 @@ gpt2_status gpt2_destroy(gpt2_ctx* c) {
   if (c->fork) hipEventDestroy(c->fork);
   if (c->join) hipEventDestroy(c->join);
   if (c->tail) hipEventDestroy(c->tail);
+  if (c->wte_dw) hipEventDestroy(c->wte_dw);
   for (auto* v : {&c->ev_ln, &c->ev_dbig, &c->ev_dqkv, &c->ev_adam})
     for (hipEvent_t e : *v)
       if (e) hipEventDestroy(e);
