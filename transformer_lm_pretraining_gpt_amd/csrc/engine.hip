@@ -534,8 +534,8 @@ gpt2_status forward(gpt2_ctx* c, const int32_t* tokens, const int32_t* targets, 
 // every weight-gradient product (with its split-K sum) and the QKV bias partial sums on the side
 // stream, each waiting for the event of the output gradient it reads. The two streams fill each
 // other's idle CUs (a product's partly filled last round of tiles, the latency-bound attention
-// backward). The main stream joins the side stream before the embedding backward, which adds to
-// the LM head's weight gradient.
+// backward). The embedding backward, which adds to the LM head's weight gradient, waits for that
+// product only; the main stream joins the whole side stream before the backward returns.
 gpt2_status backward(gpt2_ctx* c, float grad_scale, int acc) {
   const Geo& g = c->g;
   Bufs& b = c->b;
