@@ -132,6 +132,7 @@ __global__ __launch_bounds__(256) void embed_seg_kernel(int M, int d,
                                                         const float* __restrict__ dh0,
                                                         float* __restrict__ dwte,
                                                         float* __restrict__ part) {
+  constexpr int AHEAD = 8;  // rows loaded before any is added: one memory wait per 8 entries
   const int c = blockIdx.x;
   const int e0 = c * CHUNK, e1 = min(M, e0 + CHUNK);
   const int tok_prev = e0 > 0 ? tok_of(keys[e0 - 1]) : -1;
@@ -141,27 +142,45 @@ __global__ __launch_bounds__(256) void embed_seg_kernel(int M, int d,
     f32x4 acc{0, 0, 0, 0};
     int cur = tok_of(keys[e0]);
     int start = e0;
-    for (int e = e0; e <= e1; ++e) {
-      const int tok = e < e1 ? tok_of(keys[e]) : -2;
-      if (tok != cur) {
-        const bool before = start == e0 && cur == tok_prev;
-        const bool after = e == e1 && cur == tok_next;
-        if (before)
-          *reinterpret_cast<f32x4*>(part + ((int64_t)c * 2 + 0) * d + 4 * cv) = acc;
-        else if (after)
-          *reinterpret_cast<f32x4*>(part + ((int64_t)c * 2 + 1) * d + 4 * cv) = acc;
-        else {
-          f32x4* w = reinterpret_cast<f32x4*>(dwte + (int64_t)cur * d + 4 * cv);
-          *w = *w + acc;
-        }
-        if (e == e1) break;
-        acc = f32x4{0, 0, 0, 0};
-        cur = tok;
-        start = e;
+    // the run `cur` that began at `start` ends before entry e
+    auto flush = [&](int e) {
+      const bool before = start == e0 && cur == tok_prev;
+      const bool after = e == e1 && cur == tok_next;
+      if (before)
+        *reinterpret_cast<f32x4*>(part + ((int64_t)c * 2 + 0) * d + 4 * cv) = acc;
+      else if (after)
+        *reinterpret_cast<f32x4*>(part + ((int64_t)c * 2 + 1) * d + 4 * cv) = acc;
+      else {
+        f32x4* w = reinterpret_cast<f32x4*>(dwte + (int64_t)cur * d + 4 * cv);
+        *w = *w + acc;
       }
-      const int pos = (int)(keys[e] & 0xffffu);
-      acc += *reinterpret_cast<const f32x4*>(dh0 + (int64_t)pos * d + 4 * cv);
+    };
+    for (int eb = e0; eb < e1; eb += AHEAD) {
+      f32x4 row[AHEAD];
+      int tk[AHEAD];
+#pragma unroll
+      for (int j = 0; j < AHEAD; ++j) {
+        const int e = eb + j;
+        if (e < e1) {
+          const uint32_t key = keys[e];
+          tk[j] = tok_of(key);
+          row[j] = *reinterpret_cast<const f32x4*>(dh0 + (int64_t)(key & 0xffffu) * d + 4 * cv);
+        }
+      }
+#pragma unroll
+      for (int j = 0; j < AHEAD; ++j) {
+        const int e = eb + j;
+        if (e >= e1) break;
+        if (tk[j] != cur) {
+          flush(e);
+          acc = f32x4{0, 0, 0, 0};
+          cur = tk[j];
+          start = e;
+        }
+        acc += row[j];
+      }
     }
+    flush(e1);
   }
 }
 
