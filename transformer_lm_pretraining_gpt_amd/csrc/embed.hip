@@ -142,6 +142,10 @@ __global__ __launch_bounds__(256) void embed_seg_kernel(int M, int d,
     f32x4 acc{0, 0, 0, 0};
     int cur = tok_of(keys[e0]);
     int start = e0;
+    // dwte's row of the current run, loaded with the run's first entry: no other flush of this
+    // kernel writes it (a token's entries are one run, added by one chunk; runs that cross a
+    // chunk border go to the partial slots), so the value is still current at the flush
+    f32x4 wcur = *reinterpret_cast<const f32x4*>(dwte + (int64_t)cur * d + 4 * cv);
     // the run `cur` that began at `start` ends before entry e
     auto flush = [&](int e) {
       const bool before = start == e0 && cur == tok_prev;
@@ -150,13 +154,11 @@ __global__ __launch_bounds__(256) void embed_seg_kernel(int M, int d,
         *reinterpret_cast<f32x4*>(part + ((int64_t)c * 2 + 0) * d + 4 * cv) = acc;
       else if (after)
         *reinterpret_cast<f32x4*>(part + ((int64_t)c * 2 + 1) * d + 4 * cv) = acc;
-      else {
-        f32x4* w = reinterpret_cast<f32x4*>(dwte + (int64_t)cur * d + 4 * cv);
-        *w = *w + acc;
-      }
+      else
+        *reinterpret_cast<f32x4*>(dwte + (int64_t)cur * d + 4 * cv) = wcur + acc;
     };
     for (int eb = e0; eb < e1; eb += AHEAD) {
-      f32x4 row[AHEAD];
+      f32x4 row[AHEAD], wrow[AHEAD];
       int tk[AHEAD];
 #pragma unroll
       for (int j = 0; j < AHEAD; ++j) {
@@ -165,6 +167,7 @@ __global__ __launch_bounds__(256) void embed_seg_kernel(int M, int d,
           const uint32_t key = keys[e];
           tk[j] = tok_of(key);
           row[j] = *reinterpret_cast<const f32x4*>(dh0 + (int64_t)(key & 0xffffu) * d + 4 * cv);
+          wrow[j] = *reinterpret_cast<const f32x4*>(dwte + (int64_t)tk[j] * d + 4 * cv);
         }
       }
 #pragma unroll
@@ -176,6 +179,7 @@ __global__ __launch_bounds__(256) void embed_seg_kernel(int M, int d,
           acc = f32x4{0, 0, 0, 0};
           cur = tk[j];
           start = e;
+          wcur = wrow[j];
         }
         acc += row[j];
       }
