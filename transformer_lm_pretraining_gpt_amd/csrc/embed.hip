@@ -202,17 +202,32 @@ __global__ __launch_bounds__(256) void embed_fixup_kernel(int M, int d, int nchu
   const bool whole = tok_of(keys[e0]) == tok;
   if (whole && e0 > 0 && tok_of(keys[e0 - 1]) == tok) return;  // run began earlier: not the owner
   const int nv = d / 4;
+  constexpr int AHEAD = 8;  // following chunks whose pieces are loaded before any is added
   for (int cv = threadIdx.x; cv < nv; cv += 256) {
     // the run began in this chunk and continues: the seg kernel kept its head in slot 1
     f32x4 acc = *reinterpret_cast<const f32x4*>(part + ((int64_t)c * 2 + 1) * d + 4 * cv);
-    for (int k = c + 1; k < nchunks; ++k) {
-      const int k0 = k * CHUNK, k1 = min(M, k0 + CHUNK);
-      if (tok_of(keys[k0]) != tok) break;
-      acc += *reinterpret_cast<const f32x4*>(part + ((int64_t)k * 2 + 0) * d + 4 * cv);
-      if (!(k1 < M && tok_of(keys[k1 - 1]) == tok && tok_of(keys[k1]) == tok)) break;
+    const f32x4 w0 = *reinterpret_cast<const f32x4*>(dwte + (int64_t)tok * d + 4 * cv);
+    bool open = true;
+    for (int kb = c + 1; open && kb < nchunks; kb += AHEAD) {
+      f32x4 piece[AHEAD];
+#pragma unroll
+      for (int j = 0; j < AHEAD; ++j)
+        if (kb + j < nchunks)
+          piece[j] = *reinterpret_cast<const f32x4*>(part + ((int64_t)(kb + j) * 2 + 0) * d + 4 * cv);
+#pragma unroll
+      for (int j = 0; j < AHEAD; ++j) {
+        const int k = kb + j;
+        if (!open || k >= nchunks) break;
+        const int k0 = k * CHUNK, k1 = min(M, k0 + CHUNK);
+        if (tok_of(keys[k0]) != tok) {
+          open = false;
+          break;
+        }
+        acc += piece[j];
+        open = k1 < M && tok_of(keys[k1 - 1]) == tok && tok_of(keys[k1]) == tok;
+      }
     }
-    f32x4* w = reinterpret_cast<f32x4*>(dwte + (int64_t)tok * d + 4 * cv);
-    *w = *w + acc;
+    *reinterpret_cast<f32x4*>(dwte + (int64_t)tok * d + 4 * cv) = w0 + acc;
   }
 }
 
