@@ -56,6 +56,19 @@ DEV u32x4 mask_tail(u32x4 r, int j0, int V) {
   return r;
 }
 
+// The row through a buffer resource: one per-lane offset register and a scalar offset per
+// vector, instead of a 64-bit address per vector (the vectors lie 16 KB apart, beyond the reach of
+// an instruction's immediate offset); those address registers made the kernel spill.
+DEV __amdgpu_buffer_rsrc_t row_rsrc(const void* p, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), (short)0, (int)bytes, 0x00020000);
+}
+DEV u32x4 buf_ld16(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff) {
+  return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, 0));
+}
+DEV void buf_st16(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff, const u32x4& v) {
+  __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(__attribute__((ext_vector_type(4))) unsigned int, v), r, voff, soff, 0);
+}
+
 // Hide the packed registers from the optimizer between passes: unpacking again is cheap, while
 // keeping every unpacked float alive across passes would cost the occupancy this kernel needs.
 DEV void opaque(u32x4 (&reg)[MAXV]) {
@@ -85,13 +98,15 @@ __global__ __launch_bounds__(THREADS, 8) void xent_kernel(int V, int Vp, T* __re
     if (tid == 0) atomicOr(err, ERR_TARGET_RANGE);
     y = 0;  // keep the reads in bounds; the flagged result is not used
   }
+  const auto rz = row_rsrc(z, (uint32_t)Vp * sizeof(T));
+  const uint32_t voff = 16u * tid;
   u32x4 reg[MAXV];
   float mx = -INFINITY;
 #pragma unroll
   for (int k = 0; k < MAXV; ++k) {
     const int v = tid + k * THREADS;
     if (v < nvec) {
-      reg[k] = ld16(z + v * VE);
+      reg[k] = buf_ld16(rz, voff, 16u * THREADS * k);
       if (v >= nfull) reg[k] = mask_tail<T>(reg[k], v * VE, V);
       float f[VE];
       Vec<T>::unpack(reg[k], f);
@@ -134,7 +149,7 @@ __global__ __launch_bounds__(THREADS, 8) void xent_kernel(int V, int Vp, T* __re
         for (int e = 0; e < VE; ++e)
           if (e == ey) f[e] -= 1.0f;
       }
-      st16(z + v * VE, Vec<T>::pack(f));
+      buf_st16(rz, voff, 16u * THREADS * k, Vec<T>::pack(f));
     }
   }
 }
