@@ -239,7 +239,8 @@ __global__ __launch_bounds__(256) void embed_wpe_kernel(int B, int T, int d,
   if (idx >= (int64_t)T * nv) return;
   const int t = (int)(idx / nv), cv = (int)(idx % nv);
   f32x4 s{0, 0, 0, 0};
-  for (int b = 0; b < B; ++b)
+#pragma unroll 8
+  for (int b = 0; b < B; ++b)  // in b order; the unrolled loads are in flight together
     s += *reinterpret_cast<const f32x4*>(dh0 + ((int64_t)b * T + t) * d + 4 * cv);
   f32x4* w = reinterpret_cast<f32x4*>(dwpe + (int64_t)t * d + 4 * cv);
   *w = accumulate ? *w + s : s;

@@ -65,8 +65,9 @@ DEV __amdgpu_buffer_rsrc_t row_rsrc(const void* p, uint32_t bytes) {
 DEV u32x4 buf_ld16(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff) {
   return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, 0));
 }
+typedef __attribute__((ext_vector_type(4))) unsigned int uint4v;
 DEV void buf_st16(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff, const u32x4& v) {
-  __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(__attribute__((ext_vector_type(4))) unsigned int, v), r, voff, soff, 0);
+  __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(uint4v, v), r, voff, soff, 0);
 }
 
 // Hide the packed registers from the optimizer between passes: unpacking again is cheap, while
@@ -155,15 +156,19 @@ __global__ __launch_bounds__(THREADS, 8) void xent_kernel(int V, int Vp, T* __re
 }
 
 // Mean over the trained positions (ignored rows hold loss 0), and the matching gradient scale.
-__global__ __launch_bounds__(256) void loss_mean_kernel(int M, const float* __restrict__ rows,
-                                                        const int32_t* __restrict__ targets,
-                                                        float* __restrict__ out,
-                                                        float* __restrict__ out_user) {
-  __shared__ float sh[4];
-  __shared__ int shn[4];
+// One block of 1024 threads (it sits between the forward and the backward, so its latency counts):
+// each thread adds a strided set of rows, then the 16 wave sums are added in wave order.
+constexpr int MEAN_THREADS = 1024;
+__global__ __launch_bounds__(MEAN_THREADS) void loss_mean_kernel(
+    int M, const float* __restrict__ rows, const int32_t* __restrict__ targets,
+    float* __restrict__ out, float* __restrict__ out_user) {
+  constexpr int NW = MEAN_THREADS / 64;
+  __shared__ float sh[NW];
+  __shared__ int shn[NW];
   float s = 0.0f;
   int n = 0;
-  for (int i = threadIdx.x; i < M; i += 256) {
+#pragma unroll 4
+  for (int i = threadIdx.x; i < M; i += MEAN_THREADS) {
     s += rows[i];
     n += targets[i] != TARGET_IGNORE;
   }
@@ -176,8 +181,13 @@ __global__ __launch_bounds__(256) void loss_mean_kernel(int M, const float* __re
   }
   __syncthreads();
   if (threadIdx.x == 0) {
-    const int cnt = shn[0] + shn[1] + shn[2] + shn[3];
-    const float mean = cnt > 0 ? (((sh[0] + sh[1]) + sh[2]) + sh[3]) / (float)cnt : 0.0f;
+    float tot = 0.0f;
+    int cnt = 0;
+    for (int w = 0; w < NW; ++w) {
+      tot += sh[w];
+      cnt += shn[w];
+    }
+    const float mean = cnt > 0 ? tot / (float)cnt : 0.0f;
     out[0] = mean;
     out[1] = cnt > 0 ? 1.0f / (float)cnt : 0.0f;
     if (out_user) out_user[0] = mean;
@@ -202,7 +212,7 @@ hipError_t launch_xent(bool is_bf16, int M, int V, int Vp, void* logits, const i
 
 hipError_t launch_loss_mean(int M, const float* row_loss, const int32_t* targets, float* loss_out,
                             float* loss_user, hipStream_t s) {
-  hipLaunchKernelGGL(loss_mean_kernel, dim3(1), dim3(256), 0, s, M, row_loss, targets, loss_out,
-                     loss_user);
+  hipLaunchKernelGGL(loss_mean_kernel, dim3(1), dim3(MEAN_THREADS), 0, s, M, row_loss, targets,
+                     loss_out, loss_user);
   return hipGetLastError();
 }
