@@ -464,12 +464,13 @@ gpt2_status colsum(gpt2_ctx* c, const void* src, int N, float* part, hipStream_t
 // LayerNorm backward into the residual gradient; its three column partial sums (gain and shift
 // gradients, and the bias gradient of the projection that produced this residual stream) go to
 // LayerNorm slice k and are reduced with the others at the end of the backward.
+// LayerNorm backward of slot k; its launch records ev_ln[k] for the side stream.
 gpt2_status ln_backward(gpt2_ctx* c, const float* x, const float* mean, const float* rstd,
                         int64_t g_off, int has_dres, int k) {
   const Geo& g = c->g;
   HIPCHK(launch_ln_bwd(g.bf16, g.M, g.d, c->b.dtmp, x, mean, rstd, c->b.params + g_off, c->b.dres,
                        has_dres, c->b.dres_t[k], ln_part(g, c->b, k), LN_ROWS_PER_BLOCK,
-                       c->stream));
+                       c->stream, c->ev_ln[k]));
   return GPT2_OK;
 }
 
@@ -566,7 +567,6 @@ gpt2_status backward(gpt2_ctx* c, float grad_scale, int acc) {
   STEP(gemm(c, 1, 0, M, d, g.Vp, b.logits, g.Vp, W(c, g.wte), d, epi_dy, b.dtmp, d, nullptr,
             nullptr, nullptr, nullptr, grad_scale, 0.0f, 0, nullptr, inv_n));
   STEP(ln_backward(c, b.resid[g.L], b.lnf_mean, b.lnf_rstd, g.lnfg, 0, 2 * g.L));
-  HIPCHK(hipEventRecord(c->ev_ln[2 * g.L], c->stream));
   for (int l = g.L - 1; l >= 0; --l) {
     // h_{l+1} = h_mid + act W_proj + b_proj: its gradient came from LayerNorm slot kp
     const int kp = l == g.L - 1 ? 2 * g.L : 2 * (l + 1);
@@ -589,7 +589,6 @@ gpt2_status backward(gpt2_ctx* c, float grad_scale, int acc) {
     STEP(gemm_dw(c, d, 4 * d, b.ln2[l], b.dbig[l], G + g.wfc(l), acc, side));
     STEP(gemm(c, 1, 1, M, d, 4 * d, b.dbig[l], 4 * d, W(c, g.wfc(l)), 4 * d, epi_dy, b.dtmp, d));
     STEP(ln_backward(c, b.resid_mid[l], b.ln2_mean[l], b.ln2_rstd[l], g.ln2g(l), 1, 2 * l + 1));
-    HIPCHK(hipEventRecord(c->ev_ln[2 * l + 1], c->stream));
     // h_mid = h_l + att W_o + b_o
     void* dm = b.dres_t[2 * l + 1];
     HIPCHK(hipStreamWaitEvent(side, c->ev_ln[2 * l + 1], 0));
@@ -603,7 +602,6 @@ gpt2_status backward(gpt2_ctx* c, float grad_scale, int acc) {
     STEP(gemm_dw(c, d, 3 * d, b.ln1[l], b.dqkv[l], G + g.wqkv(l), acc, side));
     STEP(gemm(c, 1, 1, M, d, 3 * d, b.dqkv[l], 3 * d, W(c, g.wqkv(l)), 3 * d, epi_dy, b.dtmp, d));
     STEP(ln_backward(c, b.resid[l], b.ln1_mean[l], b.ln1_rstd[l], g.ln1g(l), 1, 2 * l));
-    HIPCHK(hipEventRecord(c->ev_ln[2 * l], c->stream));
   }
   // Every bias and LayerNorm gain/shift gradient from its partial rows, in one launch on the side
   // stream once the last LayerNorm backward has written its rows, beside the embedding backward;

@@ -69,7 +69,8 @@ hipError_t launch_ln_fwd(bool is_bf16, int M, int d, const float* x, const float
 hipError_t launch_ln_bwd(bool is_bf16, int M, int d, const void* dy, const float* x,
                          const float* mean, const float* rstd, const float* g, float* dres,
                          int has_dres, void* dres_t, float* part, int rows_per_block,
-                         hipStream_t s);
+                         hipStream_t s,
+                         hipEvent_t done = nullptr);
 int ln_bwd_blocks(int M, int rows_per_block);
 // Column partial sums of a (M, N) matrix (T or fp32) per block of rows: part[blk][N].
 hipError_t launch_colsum_partial(bool src_bf16, int M, int N, const void* src, int64_t ld,

@@ -11,6 +11,8 @@
 // partials in a fixed order, so results are bitwise reproducible.
 #include <type_traits>
 
+#include <hip/hip_ext.h>
+
 #include "common.h"
 #include "kernels.h"
 
@@ -291,21 +293,22 @@ int ln_bwd_blocks(int M, int rows_per_block) { return (M + rows_per_block - 1) /
 hipError_t launch_ln_bwd(bool is_bf16, int M, int d, const void* dy, const float* x,
                          const float* mean, const float* rstd, const float* g, float* dres,
                          int has_dres, void* dres_t, float* part, int rows_per_block,
-                         hipStream_t s) {
+                         hipStream_t s, hipEvent_t done) {
   if (M == 0) return hipSuccess;
   if (d % 4 || d > 4 * 64 * MAXV) return hipErrorInvalidValue;
   dim3 grid(ln_bwd_blocks(M, rows_per_block));
   const size_t lds = 4 * (size_t)d * sizeof(float);
   return with_nv(d, [&](auto nv) {
     constexpr int NV = decltype(nv)::value;
+    // `done`, when given, is recorded by the launch itself (no marker packet of its own)
     if (is_bf16)
-      hipLaunchKernelGGL((ln_bwd_kernel<bf16, NV>), grid, dim3(256), lds, s, M, d,
-                         static_cast<const bf16*>(dy), x, mean, rstd,
-                         g, dres, has_dres, static_cast<bf16*>(dres_t), part, rows_per_block);
+      hipExtLaunchKernelGGL((ln_bwd_kernel<bf16, NV>), grid, dim3(256), lds, s, nullptr, done, 0,
+                            M, d, static_cast<const bf16*>(dy), x, mean, rstd, g, dres, has_dres,
+                            static_cast<bf16*>(dres_t), part, rows_per_block);
     else
-      hipLaunchKernelGGL((ln_bwd_kernel<float, NV>), grid, dim3(256), lds, s, M, d,
-                         static_cast<const float*>(dy), x, mean, rstd,
-                         g, dres, has_dres, static_cast<float*>(dres_t), part, rows_per_block);
+      hipExtLaunchKernelGGL((ln_bwd_kernel<float, NV>), grid, dim3(256), lds, s, nullptr, done, 0,
+                            M, d, static_cast<const float*>(dy), x, mean, rstd, g, dres, has_dres,
+                            static_cast<float*>(dres_t), part, rows_per_block);
     return hipGetLastError();
   });
 }
