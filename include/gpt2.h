@@ -126,15 +126,28 @@ gpt2_status gpt2_clip_grad_norm(gpt2_ctx* ctx, float max_norm, float* d_norm);
 /* AdamW ([OBJ], [MEM]): t += 1, then per element
  *   m = b1 m + (1-b1) g;  v = b2 v + (1-b2) g^2;
  *   p -= lr * ( (m / (1-b1^t)) / (sqrt(v / (1-b2^t)) + eps) + wd * p ),
- * with wd = weight_decay on 2-D tensors and 0 elsewhere; refreshes the bf16 weight copy. */
+ * with wd = weight_decay on 2-D tensors and 0 elsewhere; refreshes the bf16 weight copy.
+ * The update runs on a stream internal to the context, one launch per parameter range, so that
+ * it overlaps the next forward's first layers: it is ordered before the next gpt2_forward_loss
+ * and gpt2_backward of this context (each range before its first use), before gpt2_check, the
+ * copy calls and gpt2_destroy, and before whatever the caller enqueues on its own stream after
+ * gpt2_join; NOT before other work the caller enqueues on its stream. */
 gpt2_status gpt2_adamw_step(gpt2_ctx* ctx, float lr, float beta1, float beta2, float eps,
                             float weight_decay);
 
-/* Wait for the context's stream, then report GPT2_E_DEVICE if a kernel flagged bad input since the
- * last check (and clear the flag), GPT2_E_HIP on an asynchronous HIP error, else GPT2_OK. */
+/* Make the context's stream wait (asynchronously, no host wait) for everything the context has
+ * queued on its internal stream so far (AdamW updates, weight-gradient products). After it, work
+ * the caller enqueues on that stream, e.g. a timing event, runs after the whole step. */
+gpt2_status gpt2_join(gpt2_ctx* ctx);
+
+/* Wait for the context's stream and its internal stream, then report GPT2_E_DEVICE if a kernel
+ * flagged bad input since the last check (and clear the flag), GPT2_E_HIP on an asynchronous HIP
+ * error, else GPT2_OK. */
 gpt2_status gpt2_check(gpt2_ctx* ctx);
 
-/* Free the host-side context. The arena stays the caller's. */
+/* Wait for both of the context's streams, then free the host-side context (also when a wait
+ * reports an error, which is returned as GPT2_E_HIP). The arena stays the caller's; once this
+ * returns, no work of the context touches it. */
 gpt2_status gpt2_destroy(gpt2_ctx* ctx);
 
 /* Synchronous copies between the arena and host memory, in canonical flat order, n = N floats.
@@ -147,12 +160,18 @@ gpt2_status gpt2_copy_adam_state(gpt2_ctx* ctx, int32_t set, float* host_m, floa
 /* Per-position losses of the most recent forward (batch*seq_len floats, row-major (B, T)). */
 gpt2_status gpt2_copy_row_loss(gpt2_ctx* ctx, float* host, size_t n);
 
-/* Time every launch of one kernel family over the next calls, with HIP events on the context's
- * stream: gpt2_timing_begin(ctx, family) arms it (family 0 = the LM-head forward GEMM,
- * 1 = all matrix-product GEMM launches, 2 = causal attention forward, 3 = fused cross-entropy,
- * 4 = AdamW); gpt2_timing_end synchronises and returns the summed milliseconds, the number of
- * launches timed and the summed algorithmic FLOPs (matrix products) or bytes (memory-bound
- * kernels) of those launches. At most 4096 launches are recorded per arm. */
+/* Time every launch of one kernel family over the next calls, with a pair of HIP events around
+ * each launch on the stream the launch goes to (the context's stream or its internal one):
+ * gpt2_timing_begin(ctx, family) arms it; gpt2_timing_end synchronises and returns the summed
+ * milliseconds, the number of launches timed and the summed algorithmic work of those launches:
+ * FLOPs for matrix products and attention (2 m n k per product; 4 head_dim per causal pair
+ * forward, 8 head_dim backward), bytes that must cross HBM for memory-bound kernels, 0 where no
+ * figure is kept. Families: 0 LM-head forward product, 1 every matrix product, 2 attention
+ * forward, 3 fused cross-entropy (bytes), 4 AdamW (bytes), 5 weight-gradient products (with the
+ * tied LM head's), 6 attention backward, 7 LayerNorm forward (bytes), 8 LayerNorm backward
+ * (bytes), 9 split-K sums of weight gradients (bytes), 10 bias and LayerNorm parameter column
+ * sums (bytes), 11 embedding gather, token sort and embedding backward (no work figure),
+ * 12 forward products, 13 input-gradient products. At most 4096 launches are recorded per arm. */
 gpt2_status gpt2_timing_begin(gpt2_ctx* ctx, int32_t family);
 gpt2_status gpt2_timing_end(gpt2_ctx* ctx, double* total_ms, int64_t* launches, double* work);
 

@@ -216,3 +216,17 @@ def test_attention_bf16(hd, T, H):
         g, r = got["dqkv"][:, i * d:(i + 1) * d], ref["dqkv"][:, i * d:(i + 1) * d]
         assert cosine(g, r) > 0.999, part
         assert normwise_rel(g, r) < 5e-2, part
+
+
+def test_attention_bf16_long_rows():
+    """The T = 8192 workload's attention at its full sequence length (one head of one sequence):
+    query rows of up to 8192 keys, 32 blocks of 256 queries, against the oracle's attention."""
+    torch = torch_cuda()
+    got, ref = _attn_case(torch, "bf16", 1, 8192, 1, 64, seed=8192)
+    assert normwise_rel(got["lse"], ref["lse"]) < 1e-3
+    assert cosine(got["o"], ref["o"]) > 0.9999
+    assert normwise_rel(got["o"], ref["o"]) < 2e-2
+    for i, part in enumerate(("dq", "dk", "dv")):
+        g, r = got["dqkv"][:, i * 64:(i + 1) * 64], ref["dqkv"][:, i * 64:(i + 1) * 64]
+        assert cosine(g, r) > 0.999, part
+        assert normwise_rel(g, r) < 5e-2, part

@@ -105,6 +105,78 @@ def test_bf16_full_size_sampled(name):
     model.close()
 
 
+# (sequence, trained prefix) of the full-size gradient tests: the sequence in the middle of the
+# batch where there is one, so that its entries sit inside the long sorted runs of frequent tokens
+# in the embedding backward (not only at their ends); the whole sequence where the oracle finishes
+# it in seconds, else a prefix (causality: the loss of positions < t1 depends only on tokens
+# < t1, so its gradient is the gradient of the same model over that prefix)
+FULL_TRAINED = {"gpt2_124m": (7, 1024), "gpt2_350m": (3, 1024), "gpt2_1p5b": (1, 256),
+                "gpt2_124m_t8192": (1, 2048)}
+
+
+def _check_bf16_grad(got_flat, ref_flat, ocfg, what):
+    got, ref = per_tensor(ocfg, got_flat), per_tensor(ocfg, ref_flat)
+    worst = min((cosine(got[n], ref[n]), n) for n in ref)
+    assert worst[0] >= BF16_GRAD_COS, (what, worst)
+    # cosine is blind to scale: the whole gradient's norm against the oracle's, at the loss bar
+    ng = float(np.linalg.norm(np.asarray(got_flat, np.float64)))
+    nr = float(np.linalg.norm(np.asarray(ref_flat, np.float64)))
+    assert abs(ng - nr) <= BF16_LOSS_REL * nr, (what, ng, nr)
+    assert np.all(got["wte"].reshape(ocfg.vocab_padded, -1)[ocfg.vocab:] == 0.0), what
+    return worst
+
+
+def _widen_grad(g_small, small, big):
+    """A gradient of the model with a t1-row position table in the layout of the T-row model:
+    position rows t1..T-1 (which no trained position reads) are zero."""
+    out = np.zeros(O.param_count(big), dtype=np.float64)
+    gs, gb = per_tensor(small, g_small), per_tensor(big, out)
+    for name in gs:
+        gb[name][:gs[name].size] = gs[name]
+    return out
+
+
+@pytest.mark.parametrize("name", FULL)
+def test_bf16_full_size_gradient(name):
+    """The bench launch configuration (full batch and sequence length, same tiles, split-K over all
+    batch*seq_len rows, the full token sort) against the oracle's complete gradient. Every target
+    is -1 except those of positions < t1 of one sequence b: the loss is then the mean loss of
+    those positions, every other position contributes exact zeros (sequences never see each other,
+    and a position never sees later ones), and the gradient equals the gradient of the
+    one-sequence model over the prefix x[b, :t1], which the oracle computes. The step runs twice
+    on the same batch, grad_scale 0.25 alone, then 0.75 with accumulate = 1: both the overwriting
+    and the accumulating paths are compared (0.25 g and g)."""
+    torch = torch_cuda()
+    model, ocfg, kind = make(G, PRESETS[name])
+    x, y = tokens(kind, ocfg, seed=41)
+    b, t1 = FULL_TRAINED[name]
+    ym = np.full_like(y, -1)
+    ym[b, :t1] = y[b, :t1]
+    loss1, rows1, g1 = gpu_forward_backward(torch, model, x, ym, grad_scale=0.25)
+    assert np.isfinite(loss1) and np.all(np.isfinite(g1))
+    rows1 = rows1.reshape(ocfg.batch, ocfg.seq_len)
+    keep = ym != -1
+    assert np.all(rows1[~keep] == 0.0)
+    p_small, small = truncate_params(model.params(), ocfg, t1)
+    rloss, rrows, rg_small = O.loss_and_grad(p_small.astype(np.float64), x[b:b + 1, :t1],
+                                             y[b:b + 1, :t1], small)
+    del p_small
+    rg = _widen_grad(rg_small, small, ocfg)
+    del rg_small
+    assert abs(loss1 - rloss) <= BF16_LOSS_REL * abs(rloss), (loss1, rloss)
+    assert np.abs(rows1[b, :t1] - rrows).max() < 0.1
+    wpe = per_tensor(ocfg, g1)["wpe"].reshape(ocfg.seq_len, -1)
+    assert np.all(wpe[t1:] == 0.0)
+    _check_bf16_grad(g1, 0.25 * rg, ocfg, "grad_scale 0.25")
+    del g1, wpe
+    xt, yt = torch.from_numpy(x).cuda(), torch.from_numpy(ym).cuda()
+    model.forward_loss(xt, yt)
+    model.backward(0.75, True)
+    model.check()
+    _check_bf16_grad(model.grads(), rg, ocfg, "0.25 + 0.75 accumulated")
+    model.close()
+
+
 def test_bf16_full_gradient_124m():
     """Optional (set GPT2_FULL_PARITY=1): the full GPT-2 124M bench batch against the oracle's
     complete float64 gradient (minutes of CPU time)."""
@@ -279,6 +351,51 @@ def test_full_size_masked_targets_sampled():
     assert loss1 == loss2 and np.array_equal(rows1, rows2) and np.array_equal(g1, g2)
     _, rows3, _ = gpu_forward_backward(torch, model, x, y)
     assert np.array_equal(rows3[keep], rows1[keep])
+    model.close()
+
+
+ACCUM = {
+    "fp32_tiny_padded_vocab": FP32_CASES["tiny_padded_vocab"],
+    # batch * seq_len a multiple of 64: the weight-gradient products take the direct-to-LDS path
+    # (split-K sums and the LM-head product's fp32 epilogue with beta = 1 when accumulating)
+    "bf16_small_T128": (2, 256, 4, 128, 4000, 4096, 2, "bf16", "zipf"),
+    "gpt2_124m_T256": (12, 768, 12, 256, 50257, 50304, 1, "bf16", "zipf"),
+}
+
+
+@pytest.mark.parametrize("name", sorted(ACCUM))
+def test_grad_accumulation_matches_oracle(name):
+    """Gradient accumulation as the pages train ("Criei GPT-2 do zero com uma RTX 4090", section
+    "Configuração do treinamento": 32 micro-batches per optimiser step): k micro-batches with
+    grad_scale 1/k, the first overwriting and the rest with accumulate = 1, against the mean of
+    the oracle's gradients of the k micro-batches, for k = 2 and 4; and one micro-batch with a
+    non-unit grad_scale and no accumulation against that multiple of the oracle's gradient."""
+    torch = torch_cuda()
+    model, ocfg, kind = make(G, ACCUM[name])
+    fp32 = ACCUM[name][7] == "fp32"
+    p0 = model.params().astype(np.float64)
+    batches = [tokens(kind, ocfg, seed=60 + i) for i in range(4)]
+    refs = [O.loss_and_grad(p0, x, y, ocfg) for x, y in batches]
+
+    def compare(got, ref, what):
+        if fp32:
+            G_, R_ = per_tensor(ocfg, got), per_tensor(ocfg, ref)
+            for n in R_:
+                assert normwise_rel(G_[n], R_[n]) <= FP32_GRAD_REL, (what, n)
+        else:
+            _check_bf16_grad(got, ref, ocfg, what)
+
+    for k in (2, 4):
+        for i in range(k):
+            x, y = batches[i]
+            loss, _, _ = gpu_forward_backward(torch, model, x, y, grad_scale=1.0 / k,
+                                              accumulate=i > 0)
+            bar = FP32_LOSS_REL if fp32 else BF16_LOSS_REL
+            assert abs(loss - refs[i][0]) <= bar * abs(refs[i][0]), (k, i)
+        compare(model.grads(), sum(r[2] for r in refs[:k]) / k, f"k={k}")
+    x, y = batches[1]
+    gpu_forward_backward(torch, model, x, y, grad_scale=0.37, accumulate=False)
+    compare(model.grads(), 0.37 * refs[1][2], "grad_scale 0.37")
     model.close()
 
 

@@ -373,6 +373,7 @@ struct gpt2_ctx {
   std::vector<hipEvent_t> ev_adam;
   int64_t t = 0;
   bool have_forward = false;
+  bool in_backward = false;  // which phase a matrix product belongs to (timing families)
   std::vector<AdamSeg> segs;
   // timing
   int timing_family = -1;
@@ -396,15 +397,34 @@ struct Timed {
       c->timed_work += work;
     }
   }
-  ~Timed() {
+  void stop() {
     if (on) {
       hipEventRecord(c->ev[2 * c->timed + 1], s);
       ++c->timed;
+      on = false;
     }
   }
+  ~Timed() { stop(); }
 };
 
-enum { FAM_LMHEAD = 0, FAM_GEMM = 1, FAM_ATTN = 2, FAM_XENT = 3, FAM_ADAMW = 4 };
+// Kernel families that gpt2_timing_begin can time (the numbering is the ABI's).
+enum {
+  FAM_LMHEAD = 0,     // LM-head forward product
+  FAM_GEMM = 1,       // every matrix product
+  FAM_ATTN = 2,       // attention forward
+  FAM_XENT = 3,       // fused cross-entropy
+  FAM_ADAMW = 4,      // AdamW
+  FAM_DW = 5,         // weight-gradient products (incl. the tied LM head's)
+  FAM_ATTN_BWD = 6,   // attention backward (dK/dV and dQ kernels)
+  FAM_LN_FWD = 7,     // LayerNorm forward
+  FAM_LN_BWD = 8,     // LayerNorm backward
+  FAM_SPLITK = 9,     // split-K partial sums of the weight gradients
+  FAM_COLSUM = 10,    // bias / LayerNorm parameter column sums (partials and the batched sum)
+  FAM_EMBED = 11,     // embedding gather, token sort and embedding backward
+  FAM_GEMM_FWD = 12,  // forward products (incl. the LM head)
+  FAM_GEMM_DX = 13,   // input-gradient products
+  FAM_COUNT = 14
+};
 
 const void* W(gpt2_ctx* c, int64_t off) {
   return c->g.bf16 ? (const void*)(static_cast<const char*>(c->b.shadow) + 2 * off)
@@ -426,6 +446,7 @@ gpt2_status gemm(gpt2_ctx* c, int a_kmajor, int b_kmajor, int M, int N, int K, c
   const double fl = 2.0 * M * N * K;
   Timed t1(c, FAM_GEMM, fl);
   Timed t0(c, tag == 1 ? FAM_LMHEAD : -2, fl);
+  Timed t2(c, c->in_backward ? FAM_GEMM_DX : FAM_GEMM_FWD, fl);
   HIPCHK(launch_gemm(c->g.bf16, a_kmajor, b_kmajor, pick_tile(c->g, M, N), 1, tag, p, c->stream));
   return GPT2_OK;
 }
@@ -441,6 +462,7 @@ gpt2_status gemm_dw(gpt2_ctx* c, int in, int out, const void* X, const void* dY,
   p.M = in; p.N = out; p.K = g.M; p.k_split = sp.k_split;
   p.epi = EPI_F32; p.alpha = 1.0f;
   Timed t1(c, FAM_GEMM, 2.0 * in * out * g.M, st);
+  Timed t2(c, FAM_DW, 2.0 * in * out * g.M, st);
   const int tile = g.bf16 ? TILE_256 : TILE_128;
   if (sp.splits == 1) {
     p.C = gw; p.ldc = out; p.beta = accumulate ? 1.0f : 0.0f;
@@ -448,6 +470,10 @@ gpt2_status gemm_dw(gpt2_ctx* c, int in, int out, const void* X, const void* dY,
   } else {
     p.C = c->b.splitk; p.ldc = out; p.c_split_stride = (int64_t)in * out; p.beta = 0.0f;
     HIPCHK(launch_gemm(g.bf16, 0, 0, tile, sp.splits, 0, p, st));
+    t2.stop();
+    t1.stop();
+    // reads the splits' fp32 partials, writes (and when accumulating reads) the gradient
+    Timed t3(c, FAM_SPLITK, 4.0 * in * out * (sp.splits + 1 + (accumulate ? 1 : 0)), st);
     HIPCHK(launch_splitk_reduce(c->b.splitk, sp.splits, (int64_t)in * out, in, out, gw, out, 1.0f,
                                 accumulate ? 1.0f : 0.0f, st));
   }
@@ -457,6 +483,7 @@ gpt2_status gemm_dw(gpt2_ctx* c, int in, int out, const void* X, const void* dY,
 // Column partial sums of an (M, N) matrix into `part` (reduced with the others at the end)
 gpt2_status colsum(gpt2_ctx* c, const void* src, int N, float* part, hipStream_t st) {
   const Geo& g = c->g;
+  Timed t(c, FAM_COLSUM, (double)(g.bf16 ? 2 : 4) * g.M * N, st);
   HIPCHK(launch_colsum_partial(g.bf16, g.M, N, src, N, part, COLSUM_ROWS_PER_BLOCK, st));
   return GPT2_OK;
 }
@@ -468,9 +495,24 @@ gpt2_status colsum(gpt2_ctx* c, const void* src, int N, float* part, hipStream_t
 gpt2_status ln_backward(gpt2_ctx* c, const float* x, const float* mean, const float* rstd,
                         int64_t g_off, int has_dres, int k) {
   const Geo& g = c->g;
+  // reads dy (bf16 or fp32), x and the incoming residual gradient (fp32); writes the residual
+  // gradient (fp32) and its copy in the product's element type
+  const double es = g.bf16 ? 2.0 : 4.0;
+  Timed t(c, FAM_LN_BWD, ((double)g.M * g.d) * (es + 4.0 + (has_dres ? 4.0 : 0.0) + 4.0 + es));
   HIPCHK(launch_ln_bwd(g.bf16, g.M, g.d, c->b.dtmp, x, mean, rstd, c->b.params + g_off, c->b.dres,
                        has_dres, c->b.dres_t[k], ln_part(g, c->b, k), LN_ROWS_PER_BLOCK,
                        c->stream, c->ev_ln[k]));
+  return GPT2_OK;
+}
+
+// LayerNorm forward of the residual stream x into y (bf16 or fp32) and its row statistics
+gpt2_status ln_forward(gpt2_ctx* c, const float* x, int64_t g_off, int64_t b_off, void* y,
+                       float* mean, float* rstd) {
+  const Geo& g = c->g;
+  // reads x (fp32), writes y
+  Timed t(c, FAM_LN_FWD, (double)g.M * g.d * (4.0 + (g.bf16 ? 2.0 : 4.0)));
+  HIPCHK(launch_ln_fwd(g.bf16, g.M, g.d, x, c->b.params + g_off, c->b.params + b_off, y, mean,
+                       rstd, c->stream));
   return GPT2_OK;
 }
 
@@ -488,18 +530,24 @@ gpt2_status forward(gpt2_ctx* c, const int32_t* tokens, const int32_t* targets, 
   // each parameter range is used once the last AdamW step has updated it (events of the side
   // stream; recorded already when no update is pending)
   HIPCHK(hipStreamWaitEvent(c->stream, c->ev_adam[0], 0));
-  HIPCHK(launch_embed_fwd(g.B, g.T, d, g.V, tokens, P + g.wte, P + g.wpe, b.resid[0], b.err,
-                          c->stream));
+  {
+    Timed t(c, FAM_EMBED, 0.0);
+    HIPCHK(launch_embed_fwd(g.B, g.T, d, g.V, tokens, P + g.wte, P + g.wpe, b.resid[0], b.err,
+                            c->stream));
+  }
   // The token sort (one workgroup, ~150 us) feeds only the embedding backward: it runs on the side
   // stream beside the forward's kernels, and the end of the forward waits for it.
   HIPCHK(hipEventRecord(c->fork, c->stream));
   HIPCHK(hipStreamWaitEvent(c->side, c->fork, 0));
-  HIPCHK(launch_token_sort(M, g.V, tokens, b.keys, c->side));
+  {
+    Timed t(c, FAM_EMBED, 0.0, c->side);
+    HIPCHK(launch_token_sort(M, g.V, tokens, b.keys, c->side));
+  }
   HIPCHK(hipEventRecord(c->join, c->side));
   for (int l = 0; l < g.L; ++l) {
     HIPCHK(hipStreamWaitEvent(c->stream, c->ev_adam[1 + l], 0));
-    HIPCHK(launch_ln_fwd(g.bf16, M, d, b.resid[l], P + g.ln1g(l), P + g.ln1b(l), b.ln1[l],
-                         b.ln1_mean[l], b.ln1_rstd[l], c->stream));
+    STEP(ln_forward(c, b.resid[l], g.ln1g(l), g.ln1b(l), b.ln1[l], b.ln1_mean[l],
+                    b.ln1_rstd[l]));
     STEP(gemm(c, 1, 0, M, 3 * d, d, b.ln1[l], d, W(c, g.wqkv(l)), 3 * d, EPI_STORE, b.qkv[l],
               3 * d, P + g.bqkv(l)));
     {
@@ -509,16 +557,15 @@ gpt2_status forward(gpt2_ctx* c, const int32_t* tokens, const int32_t* targets, 
     }
     STEP(gemm(c, 1, 0, M, d, d, b.att[l], d, W(c, g.wo(l)), d, EPI_BIAS_RESID, b.resid_mid[l], d,
               P + g.bo(l), b.resid[l]));
-    HIPCHK(launch_ln_fwd(g.bf16, M, d, b.resid_mid[l], P + g.ln2g(l), P + g.ln2b(l), b.ln2[l],
-                         b.ln2_mean[l], b.ln2_rstd[l], c->stream));
+    STEP(ln_forward(c, b.resid_mid[l], g.ln2g(l), g.ln2b(l), b.ln2[l], b.ln2_mean[l],
+                    b.ln2_rstd[l]));
     STEP(gemm(c, 1, 0, M, 4 * d, d, b.ln2[l], d, W(c, g.wfc(l)), 4 * d, EPI_BIAS_GELU, b.fc[l],
               4 * d, P + g.bfc(l), nullptr, b.act[l]));
     STEP(gemm(c, 1, 0, M, d, 4 * d, b.act[l], 4 * d, W(c, g.wproj(l)), d, EPI_BIAS_RESID,
               b.resid[l + 1], d, P + g.bproj(l), b.resid_mid[l]));
   }
   HIPCHK(hipStreamWaitEvent(c->stream, c->ev_adam[g.L + 1], 0));
-  HIPCHK(launch_ln_fwd(g.bf16, M, d, b.resid[g.L], P + g.lnfg, P + g.lnfb, b.lnf, b.lnf_mean,
-                       b.lnf_rstd, c->stream));
+  STEP(ln_forward(c, b.resid[g.L], g.lnfg, g.lnfb, b.lnf, b.lnf_mean, b.lnf_rstd));
   STEP(gemm(c, 1, 1, M, g.Vp, d, b.lnf, d, W(c, g.wte), d, EPI_STORE, b.logits, g.Vp, nullptr,
             nullptr, nullptr, nullptr, 1.0f, 0.0f, 1));
   {
@@ -560,7 +607,10 @@ gpt2_status backward(gpt2_ctx* c, float grad_scale, int acc) {
     p.epi = EPI_F32; p.C = G + g.wte; p.ldc = d; p.alpha = grad_scale; p.beta = acc ? 1.0f : 0.0f;
     p.alpha_scale = inv_n;
     Timed t(c, FAM_GEMM, 2.0 * g.Vp * d * M, side);
+    Timed t2(c, FAM_DW, 2.0 * g.Vp * d * M, side);
     HIPCHK(launch_gemm(g.bf16, 0, 0, pick_tile(g, g.Vp, d), 1, 0, p, side));
+    t2.stop();
+    t.stop();
     HIPCHK(hipEventRecord(c->wte_dw, side));
   }
   const int epi_dy = g.bf16 ? EPI_STORE : EPI_F32;
@@ -594,8 +644,12 @@ gpt2_status backward(gpt2_ctx* c, float grad_scale, int acc) {
     HIPCHK(hipStreamWaitEvent(side, c->ev_ln[2 * l + 1], 0));
     STEP(gemm_dw(c, d, d, b.att[l], dm, G + g.wo(l), acc, side));
     STEP(gemm(c, 1, 1, M, d, d, dm, d, W(c, g.wo(l)), d, EPI_STORE, b.datt, d));
-    HIPCHK(launch_attn_bwd(g.bf16, g.B, g.T, g.H, g.hd, b.qkv[l], b.att[l], b.lse[l], b.datt,
-                           b.dqkv[l], b.dsum, c->stream));
+    {
+      // counted work: dV, dP, dQ and dK, each 2 hd FLOPs per causal (query, key) pair
+      Timed t(c, FAM_ATTN_BWD, 8.0 * g.B * g.H * g.hd * ((double)g.T * (g.T + 1) / 2));
+      HIPCHK(launch_attn_bwd(g.bf16, g.B, g.T, g.H, g.hd, b.qkv[l], b.att[l], b.lse[l], b.datt,
+                             b.dqkv[l], b.dsum, c->stream));
+    }
     HIPCHK(hipEventRecord(c->ev_dqkv[l], c->stream));
     HIPCHK(hipStreamWaitEvent(side, c->ev_dqkv[l], 0));
     STEP(colsum(c, b.dqkv[l], 3 * d, qkv_part(g, b, l), side));
@@ -609,9 +663,13 @@ gpt2_status backward(gpt2_ctx* c, float grad_scale, int acc) {
   // ends. The embedding backward adds into the tied wte gradient, so it waits only for the LM
   // head's weight gradient, not for the side stream's last weight gradients.
   HIPCHK(hipStreamWaitEvent(side, c->ev_ln[0], 0));
-  HIPCHK(launch_colsum_reduce_batch(b.coltasks, b.ncoltasks, b.ncolblocks, acc, side));
+  {
+    Timed t(c, FAM_COLSUM, 4.0 * (double)col_layout(g).total, side);
+    HIPCHK(launch_colsum_reduce_batch(b.coltasks, b.ncoltasks, b.ncolblocks, acc, side));
+  }
   HIPCHK(hipEventRecord(c->tail, side));
   HIPCHK(hipStreamWaitEvent(c->stream, c->wte_dw, 0));
+  Timed te(c, FAM_EMBED, 0.0);
   HIPCHK(launch_embed_bwd(g.B, g.T, d, b.keys, b.dres, G + g.wte, G + g.wpe, acc, b.segpart,
                           c->stream));
   HIPCHK(hipStreamWaitEvent(c->stream, c->tail, 0));
@@ -736,7 +794,10 @@ gpt2_status gpt2_backward(gpt2_ctx* c, float grad_scale, int32_t accumulate) {
   if (!c->have_forward) return fail(GPT2_E_STATE, "backward needs a forward first");
   if (accumulate != 0 && accumulate != 1) return fail(GPT2_E_INVALID, "accumulate must be 0 or 1");
   if (!isfinite(grad_scale)) return fail(GPT2_E_INVALID, "grad_scale must be finite");
-  return backward(c, grad_scale, accumulate);
+  c->in_backward = true;
+  const gpt2_status s = backward(c, grad_scale, accumulate);
+  c->in_backward = false;
+  return s;
 }
 
 gpt2_status gpt2_adamw_step(gpt2_ctx* c, float lr, float beta1, float beta2, float eps,
@@ -792,7 +853,9 @@ gpt2_status gpt2_clip_grad_norm(gpt2_ctx* c, float max_norm, float* d_norm) {
 
 gpt2_status gpt2_check(gpt2_ctx* c) {
   STEP(check_ctx(c));
+  // the side stream carries AdamW and the weight-gradient products: wait for both streams
   HIPCHK(hipStreamSynchronize(c->stream));
+  HIPCHK(hipStreamSynchronize(c->side));
   int err = 0;
   HIPCHK(hipMemcpy(&err, c->b.err, sizeof(int), hipMemcpyDeviceToHost));
   if (err) {
@@ -808,6 +871,10 @@ gpt2_status gpt2_check(gpt2_ctx* c) {
 
 gpt2_status gpt2_destroy(gpt2_ctx* c) {
   if (!c) return fail(GPT2_E_INVALID, "context is NULL");
+  // work queued on either stream may still write into the caller's arena: let it finish before
+  // the caller can free or reuse the arena (errors are reported but the context is still freed)
+  const hipError_t e_main = hipStreamSynchronize(c->stream);
+  const hipError_t e_side = c->side ? hipStreamSynchronize(c->side) : hipSuccess;
   for (hipEvent_t e : c->ev) hipEventDestroy(e);
   if (c->fork) hipEventDestroy(c->fork);
   if (c->join) hipEventDestroy(c->join);
@@ -818,6 +885,16 @@ gpt2_status gpt2_destroy(gpt2_ctx* c) {
       if (e) hipEventDestroy(e);
   if (c->side) hipStreamDestroy(c->side);
   delete c;
+  if (e_main != hipSuccess || e_side != hipSuccess)
+    return fail(GPT2_E_HIP, std::string("stream synchronisation before destroy failed: ") +
+                                hipGetErrorString(e_main != hipSuccess ? e_main : e_side));
+  return GPT2_OK;
+}
+
+gpt2_status gpt2_join(gpt2_ctx* c) {
+  STEP(check_ctx(c));
+  HIPCHK(hipEventRecord(c->tail, c->side));
+  HIPCHK(hipStreamWaitEvent(c->stream, c->tail, 0));
   return GPT2_OK;
 }
 
@@ -875,7 +952,8 @@ gpt2_status gpt2_copy_row_loss(gpt2_ctx* c, float* host, size_t n) {
 
 gpt2_status gpt2_timing_begin(gpt2_ctx* c, int32_t family) {
   STEP(check_ctx(c));
-  if (family < 0 || family > 4) return fail(GPT2_E_INVALID, "family must be 0..4");
+  if (family < 0 || family >= FAM_COUNT)
+    return fail(GPT2_E_INVALID, "family must be 0.." + std::to_string(FAM_COUNT - 1));
   if (c->ev.empty()) {
     c->ev.resize(2 * TIMING_CAP);
     for (auto& e : c->ev) HIPCHK(hipEventCreate(&e));

@@ -19,7 +19,9 @@ GPT2_OK, GPT2_E_INVALID, GPT2_E_NOMEM, GPT2_E_HIP, GPT2_E_STATE, GPT2_E_UNSUPPOR
 STATUS_NAMES = {0: "OK", -1: "INVALID", -2: "NOMEM", -3: "HIP", -4: "STATE", -5: "UNSUPPORTED",
                 -6: "DEVICE"}
 FP32, BF16 = 0, 1
-TIMING_FAMILIES = {"lm_head_gemm": 0, "gemm": 1, "attention_fwd": 2, "xent": 3, "adamw": 4}
+TIMING_FAMILIES = {"lm_head_gemm": 0, "gemm": 1, "attention_fwd": 2, "xent": 3, "adamw": 4,
+                   "gemm_dw": 5, "attention_bwd": 6, "ln_fwd": 7, "ln_bwd": 8, "splitk_sum": 9,
+                   "colsum": 10, "embedding": 11, "gemm_fwd": 12, "gemm_dx": 13}
 
 
 class Config(ctypes.Structure):
@@ -72,6 +74,7 @@ def load_library(path: str | None = None):
         "gpt2_adamw_step": (st, [c_void_p, c_float, c_float, c_float, c_float, c_float]),
         "gpt2_clip_grad_norm": (st, [c_void_p, c_float, c_void_p]),
         "gpt2_check": (st, [c_void_p]),
+        "gpt2_join": (st, [c_void_p]),
         "gpt2_destroy": (st, [c_void_p]),
         "gpt2_copy_params": (st, [c_void_p, c_int32, c_void_p, c_size_t]),
         "gpt2_copy_grads": (st, [c_void_p, c_int32, c_void_p, c_size_t]),
@@ -161,6 +164,11 @@ class GPT2:
 
     def check(self):
         _check(self.lib.gpt2_check(self.ctx))
+
+    def join(self):
+        """Order torch's current stream after everything the context queued on its internal
+        stream (AdamW, weight gradients), without a host wait."""
+        _check(self.lib.gpt2_join(self.ctx))
 
     # ---- synchronous host copies ----
     def params(self) -> np.ndarray:
