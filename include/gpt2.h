@@ -227,6 +227,21 @@ gpt2_status gpt2_op_attention_backward(int32_t precision, int32_t batch, int32_t
                                        const void* d_out, const float* d_lse, const void* d_dout,
                                        void* d_dqkv, float* d_scratch, void* hip_stream);
 
+/* gpt2_op_attention_backward for callers that cannot allocate device memory (code under HIP
+ * graph capture, tight serving loops, harnesses that forbid hipMalloc): the same kernels and the
+ * same results, with the 2*batch*n_head*seq_len floats of scratch taken from a fixed array inside
+ * the library (4 MiB per GPU, held by each GPU it runs on until the process ends) instead of
+ * d_scratch. It calls no hipMalloc/hipFree and no allocating routine. GPT2_E_UNSUPPORTED when
+ * 2*batch*n_head*seq_len > 1048576 (batch*n_head*seq_len > 524288). Every call on one GPU shares
+ * that GPU's array: calls that overlap in time on one GPU (on different streams, or from several
+ * threads without ordering) race and give wrong results; calls ordered on one stream are safe.
+ * Other arguments, layouts and errors as gpt2_op_attention_backward. Asynchronous on hip_stream. */
+gpt2_status gpt2_op_attention_backward_noalloc(int32_t precision, int32_t batch, int32_t seq_len,
+                                               int32_t n_head, int32_t head_dim,
+                                               const void* d_qkv, const void* d_out,
+                                               const float* d_lse, const void* d_dout,
+                                               void* d_dqkv, void* hip_stream);
+
 #ifdef __cplusplus
 }
 #endif

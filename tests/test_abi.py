@@ -113,5 +113,13 @@ def test_null_context_and_ops_are_rejected(lib):
     assert epi(1, 1, 8, 12, 8, 16, 8, 16, 8, 0, 16, None, 16, None, None, 1.0, None) == G.GPT2_E_UNSUPPORTED
     assert epi(1, 1, 8, 8, 8, 16, 8, 24, 8, 0, 16, None, 8, None, None, 1.0, None) == G.GPT2_E_UNSUPPORTED
     assert lib.gpt2_op_attention_forward(1, 1, 8, 1, 48, 16, 16, 16, None) == G.GPT2_E_UNSUPPORTED
+    # the fixed-scratch attention backward: NULL buffers, and sizes beyond its array, are refused
+    # before any GPU work
+    noalloc = lib.gpt2_op_attention_backward_noalloc
+    assert noalloc(1, 1, 64, 1, 64, None, 16, 16, 16, 16, None) == G.GPT2_E_INVALID
+    assert noalloc(1, 1, 64, 1, 48, 16, 16, 16, 16, 16, None) == G.GPT2_E_UNSUPPORTED
+    assert noalloc(1, 512, 1025, 1, 64, 16, 16, 16, 16, 16, None) == G.GPT2_E_UNSUPPORTED
+    assert b"exceed" in lib.gpt2_last_error()
+    assert lib.gpt2_join(None) == G.GPT2_E_INVALID
     pc = ctypes.c_size_t()
     assert lib.gpt2_param_count(None, ctypes.byref(pc)) == G.GPT2_E_INVALID

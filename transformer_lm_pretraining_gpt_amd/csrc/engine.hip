@@ -10,6 +10,7 @@
 #include <string.h>
 
 #include <algorithm>
+#include <mutex>
 #include <string>
 #include <vector>
 
@@ -1066,6 +1067,68 @@ gpt2_status gpt2_op_attention_backward(int32_t precision, int32_t batch, int32_t
     return fail(GPT2_E_INVALID, "NULL buffer");
   HIPCHK(launch_attn_bwd(precision == GPT2_BF16, batch, seq_len, n_head, head_dim, d_qkv, d_out,
                          d_lse, d_dout, d_dqkv, d_scratch, static_cast<hipStream_t>(hip_stream)));
+  return GPT2_OK;
+}
+
+}  // extern "C"
+
+// ---------------------------------------------------------------- attention backward, no alloc
+// The workspace of gpt2_op_attention_backward_noalloc: the attention backward's per-row pairs
+// {log-sum-exp, D = rowsum(dO o O)} (2 floats per (batch, head, position)), written by its first
+// kernel and read by its second within one call, so nothing in it has to start at zero. Each GPU
+// the library runs on holds its own copy until the process ends. Host code never uses the
+// array's name as an address (on the host it is only a stand-in for the symbol): the device
+// address comes from hipGetSymbolAddress, looked up once per device with that device current.
+namespace {
+constexpr int64_t NOALLOC_ATTN_FLOATS = int64_t(1) << 20;  // 4 MiB: batch*n_head*seq_len <= 2^19
+static __device__ __align__(256) float scratch[NOALLOC_ATTN_FLOATS];
+
+std::mutex g_scratch_mu;
+std::vector<float*> g_scratch_dev;  // device address of `scratch`, per device id
+
+gpt2_status scratch_for_stream(hipStream_t st, float** out) {
+  int cur = 0;
+  HIPCHK(hipGetDevice(&cur));
+  int dev = cur;
+  if (st) HIPCHK(hipStreamGetDevice(st, &dev));
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if ((int)g_scratch_dev.size() <= dev) g_scratch_dev.resize(dev + 1, nullptr);
+  if (!g_scratch_dev[dev]) {
+    if (dev != cur) HIPCHK(hipSetDevice(dev));
+    void* p = nullptr;
+    const hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (dev != cur) HIPCHK(hipSetDevice(cur));
+    if (e != hipSuccess)
+      return fail(GPT2_E_HIP, std::string("hipGetSymbolAddress(scratch) failed: ") +
+                                  hipGetErrorString(e));
+    g_scratch_dev[dev] = static_cast<float*>(p);
+  }
+  *out = g_scratch_dev[dev];
+  return GPT2_OK;
+}
+}  // namespace
+
+extern "C" {
+
+gpt2_status gpt2_op_attention_backward_noalloc(int32_t precision, int32_t batch, int32_t seq_len,
+                                               int32_t n_head, int32_t head_dim,
+                                               const void* d_qkv, const void* d_out,
+                                               const float* d_lse, const void* d_dout,
+                                               void* d_dqkv, void* hip_stream) {
+  STEP(attn_args(precision, batch, seq_len, n_head, head_dim));
+  if (!d_qkv || !d_out || !d_lse || !d_dout || !d_dqkv) return fail(GPT2_E_INVALID, "NULL buffer");
+  const int64_t need = 2 * (int64_t)batch * n_head * seq_len;
+  if (need > NOALLOC_ATTN_FLOATS)
+    return fail(GPT2_E_UNSUPPORTED,
+                "gpt2_op_attention_backward_noalloc: 2*batch*n_head*seq_len = " +
+                    std::to_string(need) + " floats of scratch exceed its fixed " +
+                    std::to_string(NOALLOC_ATTN_FLOATS) +
+                    "; use gpt2_op_attention_backward with a workspace");
+  const hipStream_t st = static_cast<hipStream_t>(hip_stream);
+  float* ws = nullptr;
+  STEP(scratch_for_stream(st, &ws));
+  HIPCHK(launch_attn_bwd(precision == GPT2_BF16, batch, seq_len, n_head, head_dim, d_qkv, d_out,
+                         d_lse, d_dout, d_dqkv, ws, st));
   return GPT2_OK;
 }
 

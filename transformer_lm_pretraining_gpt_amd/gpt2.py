@@ -95,6 +95,9 @@ def load_library(path: str | None = None):
         "gpt2_op_attention_backward": (st, [c_int32, c_int32, c_int32, c_int32, c_int32, c_void_p,
                                             c_void_p, c_void_p, c_void_p, c_void_p, c_void_p,
                                             c_void_p]),
+        "gpt2_op_attention_backward_noalloc": (st, [c_int32, c_int32, c_int32, c_int32, c_int32,
+                                                    c_void_p, c_void_p, c_void_p, c_void_p,
+                                                    c_void_p, c_void_p]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(lib, name)
@@ -275,3 +278,15 @@ def op_attention_backward(qkv, out, lse, dout, dqkv, scratch, batch, seq_len, n_
                                           out.data_ptr(), lse.data_ptr(), dout.data_ptr(),
                                           dqkv.data_ptr(), scratch.data_ptr(),
                                           torch.cuda.current_stream().cuda_stream))
+
+
+def op_attention_backward_noalloc(qkv, out, lse, dout, dqkv, batch, seq_len, n_head, head_dim,
+                                  precision="bf16"):
+    """The attention backward with the library's fixed scratch instead of a caller workspace."""
+    import torch
+    lib = load_library()
+    prec = BF16 if precision == "bf16" else FP32
+    _check(lib.gpt2_op_attention_backward_noalloc(prec, batch, seq_len, n_head, head_dim,
+                                                  _ptr(qkv), _ptr(out), _ptr(lse), _ptr(dout),
+                                                  _ptr(dqkv),
+                                                  torch.cuda.current_stream().cuda_stream))
