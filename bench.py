@@ -302,7 +302,7 @@ def main():
     # ---- per-family kernel timing, then the roofline of the family that takes the most time ----
     fam_steps = 3
     kernels = {}
-    for fam, unit, bound in FAMILIES:
+    for fam, unit, bound in (() if args.no_breakdown else FAMILIES):
         ms, n, work = W.family(fam, args.warmup, fam_steps)
         if n:
             kernels[fam] = rate_entry(ms, n, work, unit, bound, fam_steps, PEAK_BF16_FLOPS)
@@ -313,7 +313,9 @@ def main():
                            "second stream beside the main stream's chain, so these in-step "
                            "durations include time spent sharing CUs and their sum exceeds the "
                            "step")
-    dom = max((f for f in kernels if "frac" in kernels[f]), key=lambda f: kernels[f]["ms_per_step"])
+    # without the breakdown the weight-gradient family (the largest in every measurement so far)
+    dom = max((f for f in kernels if "frac" in kernels[f]), key=lambda f: kernels[f]["ms_per_step"],
+              default="gemm_dw")
     unit = dict((f, u) for f, u, _ in FAMILIES)[dom]
     bound = dict((f, b) for f, _, b in FAMILIES)[dom]
     ms, n, work = W.family(dom, args.warmup, args.steps)

@@ -554,7 +554,7 @@ DEV void epilogue_gelu_bwd_bf16(const f32x16 (&acc)[MB][NB], const GemmParams& p
 
 template <int EPI, int MB, int NB>
 DEV void epilogue_rows(const f32x16 (&acc)[MB][NB], const GemmParams& p, float* buf, int row0,
-                       int col0, int lane) {
+                       int col0, int lane, int z) {
   constexpr int WN = NB * 32;
   constexpr int PITCH = epi_pitch<NB>();
   constexpr int V4 = WN / 4;     // float4 per row
@@ -562,7 +562,7 @@ DEV void epilogue_rows(const f32x16 (&acc)[MB][NB], const GemmParams& p, float* 
   static_assert(8 % RPP == 0, "whole passes over the 8 rows");
   const int h = lane >> 5, l32 = lane & 31;
   float* cf = static_cast<float*>(p.C);
-  if (EPI == EPI_F32) cf += (int64_t)blockIdx.z * p.c_split_stride;
+  if (EPI == EPI_F32) cf += (int64_t)z * p.c_split_stride;
 #pragma unroll
   for (int i = 0; i < MB; ++i) {
 #pragma unroll
@@ -772,62 +772,75 @@ __global__ __launch_bounds__(64 * NW, MINB) void gemm_dma_kernel(GemmParams p) {
 
   const int tiles_m = (p.M + BM - 1) / BM, tiles_n = (p.N + BN - 1) / BN;
   const int nblk = tiles_m * tiles_n;
-  // Work items are output tiles in grouped order (GROUP row-tiles walked column by column). Block
-  // b runs on XCD b mod 8; when the grid is a multiple of 8, XCD x owns the contiguous run of
-  // items [x * per_xcd, (x + 1) * per_xcd) and its G/8 blocks stride through it, so each XCD's L2
-  // keeps its own row panels of A and streams the columns of B once.
+  // Work items are (K split, output tile) pairs, split-major: item = z * nblk + tile. Block b runs
+  // on XCD b mod 8; when the grid is a multiple of 8, XCD x owns the contiguous run of items
+  // [x * per_xcd, (x + 1) * per_xcd) and its G/8 blocks stride through it, so the blocks that
+  // run together on one XCD share the K range of a split and the operand panels of neighbouring
+  // tiles, and each XCD's L2 serves those panels to all of them.
+  const int nitems = nblk * p.splits;
   const int G = gridDim.x;
   const int b = blockIdx.x;
   int w, w_end, stride;
   if ((G & 7) == 0) {
-    const int per_xcd = (nblk + 7) >> 3;
+    const int per_xcd = (nitems + 7) >> 3;
     w = (b & 7) * per_xcd + (b >> 3);
-    w_end = min(nblk, ((b & 7) + 1) * per_xcd);
+    w_end = min(nitems, ((b & 7) + 1) * per_xcd);
     stride = G >> 3;
   } else {
     w = b;
-    w_end = nblk;
+    w_end = nitems;
     stride = G;
   }
   if (w >= w_end) return;
+  // Tile order within a split: GROUP row-tiles walked column by column; for weight gradients
+  // (both operands read k-row by k-row) with few column tiles, column tiles fastest instead, so
+  // the tiles that share a row panel of A (the largest operand there, e.g. the LM head's logit
+  // gradient) run side by side and read it once through L2.
+  const bool n_fast = AK == 0 && tiles_n <= 8;
   const int GROUP = tiles_m <= 8 ? tiles_m : (tiles_m + 7) / 8;
   const int in_group = GROUP * tiles_n;
-  const int k_begin = blockIdx.z * p.k_split;
-  const int k_end = min(p.K, k_begin + p.k_split);
-  const int nk = (k_end - k_begin) / KT;
 
   const bf16* A = static_cast<const bf16*>(p.A);
   const bf16* B = static_cast<const bf16*>(p.B);
   const int wm0 = (wave / WGN) * WM, wn0 = (wave % WGN) * WN;
 
-  // output tile of work item w
-  auto tile_origin = [&](int item, int& m0, int& n0) {
-    const int g = item / in_group;
-    const int first_m = g * GROUP;
-    const int gsize = min(tiles_m - first_m, GROUP);
-    m0 = (first_m + (item % in_group) % gsize) * BM;
-    n0 = ((item % in_group) / gsize) * BN;
+  // output tile, first k and slab count of work item `item`, and its split z
+  auto item_of = [&](int item, int& m0, int& n0, int& kb, int& nk, int& z) {
+    z = item / nblk;
+    const int t = item - z * nblk;
+    if (n_fast) {
+      m0 = (t / tiles_n) * BM;
+      n0 = (t % tiles_n) * BN;
+    } else {
+      const int g = t / in_group;
+      const int first_m = g * GROUP;
+      const int gsize = min(tiles_m - first_m, GROUP);
+      m0 = (first_m + (t % in_group) % gsize) * BM;
+      n0 = ((t % in_group) / gsize) * BN;
+    }
+    kb = z * p.k_split;
+    nk = (min(p.K, kb + p.k_split) - kb) / KT;
   };
   uint32_t offa[TA::PER_WAVE], offb[TB::PER_WAVE];  // this wave's load offsets for the tile
-  // whole slab `ks` of the tile at (m0, n0) into stage `st`
-  auto issue = [&](int m0, int n0, int ks, int st) {
+  // whole slab `ks` of the item at (m0, n0) with first k kb into stage `st`
+  auto issue = [&](int m0, int n0, int kb, int ks, int st) {
     char* dst = smem + st * STAGE;
-    const __amdgpu_buffer_rsrc_t ra = TA::slab(A, p.lda, m0, k_begin + ks * KT);
-    const __amdgpu_buffer_rsrc_t rb = TB::slab(B, p.ldb, n0, k_begin + ks * KT);
+    const __amdgpu_buffer_rsrc_t ra = TA::slab(A, p.lda, m0, kb + ks * KT);
+    const __amdgpu_buffer_rsrc_t rb = TB::slab(B, p.ldb, n0, kb + ks * KT);
 #pragma unroll
     for (int i = 0; i < TA::PER_WAVE; ++i) TA::issue(ra, offa, i, dst, wave);
 #pragma unroll
     for (int i = 0; i < TB::PER_WAVE; ++i) TB::issue(rb, offb, i, dst + BM * RB, wave);
   };
 
-  int m0, n0;
-  tile_origin(w, m0, n0);
+  int m0, n0, kb, nk, z;
+  item_of(w, m0, n0, kb, nk, z);
   TA::offsets(offa, p.lda, m0, p.M, wave, lane);
   TB::offsets(offb, p.ldb, n0, p.N, wave, lane);
   int base = 0;  // stage of this tile's slab 0
 #pragma unroll
   for (int s = 0; s < NSTAGE - 1; ++s)
-    if (s < nk) issue(m0, n0, s, s);
+    if (s < nk) issue(m0, n0, kb, s, s);
 
   while (true) {
     f32x16 acc[MB][NB];
@@ -858,7 +871,7 @@ __global__ __launch_bounds__(64 * NW, MINB) void gemm_dma_kernel(GemmParams p) {
         char* dst = smem + ((base + nxt) % NSTAGE) * STAGE;
         slab_mma_next<true, true, TA, TB, MB, NB, KSTEPS, LW, NSTAGE - 2>(
             acc, fa, fb, sa, sa + BM * RB, na, na + BM * RB, NSTAGE - 2, wm0, wn0, lane, wave,
-            TA::slab(A, p.lda, m0, k_begin + nxt * KT), TB::slab(B, p.ldb, n0, k_begin + nxt * KT),
+            TA::slab(A, p.lda, m0, kb + nxt * KT), TB::slab(B, p.ldb, n0, kb + nxt * KT),
             offa, offb, dst, dst + BM * RB);
       }
       const __amdgpu_buffer_rsrc_t unused = buffer_at(A);  // no loads left for this tile
@@ -883,8 +896,8 @@ __global__ __launch_bounds__(64 * NW, MINB) void gemm_dma_kernel(GemmParams p) {
         const int nxt = kt + NSTAGE - 1;
         char* dst = smem + ((base + nxt) % NSTAGE) * STAGE;
         slab_mma<true, TA, TB, MB, NB, KSTEPS>(
-            acc, sa, sa + BM * RB, wm0, wn0, lane, wave, TA::slab(A, p.lda, m0, k_begin + nxt * KT),
-            TB::slab(B, p.ldb, n0, k_begin + nxt * KT), offa, offb, dst, dst + BM * RB);
+            acc, sa, sa + BM * RB, wm0, wn0, lane, wave, TA::slab(A, p.lda, m0, kb + nxt * KT),
+            TB::slab(B, p.ldb, n0, kb + nxt * KT), offa, offb, dst, dst + BM * RB);
       }
       for (int kt = nmain; kt < nk; ++kt) {
         wait_slabs<LW, NSTAGE - 2>(nk - 1 - kt);
@@ -901,14 +914,14 @@ __global__ __launch_bounds__(64 * NW, MINB) void gemm_dma_kernel(GemmParams p) {
     const int last = (base + nk + NSTAGE - 1) % NSTAGE;
     const int nbase = (base + nk) % NSTAGE;
     const int wnext = w + stride;
-    int m1 = 0, n1 = 0;
+    int m1 = 0, n1 = 0, kb1 = 0, nk1 = 0, z1 = 0;
     if (wnext < w_end) {
-      tile_origin(wnext, m1, n1);
+      item_of(wnext, m1, n1, kb1, nk1, z1);
       TA::offsets(offa, p.lda, m1, p.M, wave, lane);
       TB::offsets(offb, p.ldb, n1, p.N, wave, lane);
 #pragma unroll
       for (int s = 0; s < NSTAGE - 1; ++s)
-        if (s < nk) issue(m1, n1, s, (nbase + s) % NSTAGE);
+        if (s < nk1) issue(m1, n1, kb1, s, (nbase + s) % NSTAGE);
     }
     float* buf = reinterpret_cast<float*>(smem + last * STAGE + wave * epi_wave_bytes<NB>());
     const int row0 = m0 + wm0, col0 = n0 + wn0;
@@ -918,26 +931,29 @@ __global__ __launch_bounds__(64 * NW, MINB) void gemm_dma_kernel(GemmParams p) {
       case EPI_STORE:
         if constexpr (NB == 2) epilogue_bf16<EPI_STORE, MB, NB, TAG == 1>(acc, p, buf16, row0, col0, lane);
         else if constexpr (NB == 3) epilogue_bf16_96<MB, NB>(acc, p, buf16, row0, col0, lane);
-        else epilogue_rows<EPI_STORE, MB, NB>(acc, p, buf, row0, col0, lane);
+        else epilogue_rows<EPI_STORE, MB, NB>(acc, p, buf, row0, col0, lane, z);
         break;
       case EPI_BIAS_GELU:
         if constexpr (NB == 2) epilogue_bf16<EPI_BIAS_GELU, MB, NB, false>(acc, p, buf16, row0, col0, lane);
-        else epilogue_rows<EPI_BIAS_GELU, MB, NB>(acc, p, buf, row0, col0, lane);
+        else epilogue_rows<EPI_BIAS_GELU, MB, NB>(acc, p, buf, row0, col0, lane, z);
         break;
       case EPI_BIAS_RESID:
         if constexpr (NB == 3) epilogue_resid_96<MB, NB>(acc, p, buf, row0, col0, lane);
-        else epilogue_rows<EPI_BIAS_RESID, MB, NB>(acc, p, buf, row0, col0, lane);
+        else epilogue_rows<EPI_BIAS_RESID, MB, NB>(acc, p, buf, row0, col0, lane, z);
         break;
       case EPI_GELU_BWD:
         if constexpr (NB == 2) epilogue_gelu_bwd_bf16<MB, NB>(acc, p, buf16, row0, col0, lane);
-        else epilogue_rows<EPI_GELU_BWD, MB, NB>(acc, p, buf, row0, col0, lane);
+        else epilogue_rows<EPI_GELU_BWD, MB, NB>(acc, p, buf, row0, col0, lane, z);
         break;
-      default: epilogue_rows<EPI_F32, MB, NB>(acc, p, buf, row0, col0, lane); break;
+      default: epilogue_rows<EPI_F32, MB, NB>(acc, p, buf, row0, col0, lane, z); break;
     }
     if (wnext >= w_end) break;
     w = wnext;
     m0 = m1;
     n0 = n1;
+    kb = kb1;
+    nk = nk1;
+    z = z1;
     base = nbase;
   }
 }
@@ -992,12 +1008,17 @@ int resident_blocks(K kernel, int nt) {
   return std::max(1, cus * std::max(per_cu, 1));
 }
 
+// One block per resident slot at most, over the tiles x splits work items; rounded up to a multiple
+// of 8 blocks (blocks past the items exit at once) so that every XCD gets its own run of items.
 template <void (*KERNEL)(GemmParams), int NT = THREADS>
 hipError_t launch_persistent(int tiles, int splits, const GemmParams& p, hipStream_t s) {
   static const int resident = resident_blocks(KERNEL, NT);  // one value per kernel
-  const int per_z = std::max(1, resident / splits);
-  dim3 grid(std::min(tiles, per_z), 1, splits), block(NT);
-  hipLaunchKernelGGL(KERNEL, grid, block, 0, s, p);
+  const int items = tiles * splits;
+  int g = std::min(items, resident);
+  if (g > 8 && resident % 8 == 0) g = std::min(resident, (g + 7) / 8 * 8);
+  GemmParams q = p;
+  q.splits = splits;
+  hipLaunchKernelGGL(KERNEL, dim3(g), dim3(NT), 0, s, q);
   return hipGetLastError();
 }
 

@@ -35,6 +35,8 @@ struct GemmParams {
   // EPI_GELU_BWD on the direct-to-LDS path with 64-column wave tiles only: when set, column sums
   // of the bf16 output over each 128-row block of a wave tile go to colsum[(row / 128) * N + col]
   float* colsum;
+  // number of K splits of the direct-to-LDS kernel's work items (set by the launcher)
+  int splits;
 };
 
 enum GemmTile { TILE_128 = 0, TILE_256 = 1, TILE_128x384 = 2 };
