@@ -93,7 +93,7 @@ gpt2_status gpt2_param_count(const gpt2_config* cfg, size_t* n);
  * step count t = 0. The context never allocates device memory; it only holds views into the
  * arena. GPT2_E_NOMEM if arena_bytes is too small, GPT2_E_UNSUPPORTED for valid geometry the
  * kernels do not cover (head_dim not 16/32/64, d_model > 2048 or not a multiple of 8,
- * batch*seq_len > 16384, fp32 with vocab_padded > 32768). */
+ * batch*seq_len > 65536, fp32 with vocab_padded > 32768). */
 gpt2_status gpt2_init(const gpt2_config* cfg, void* d_arena, size_t arena_bytes, void* hip_stream,
                       gpt2_ctx** out);
 

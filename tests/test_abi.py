@@ -70,7 +70,7 @@ def test_flops_per_token_matches_oracle_tally_form():
     ("reserved", 1, G.GPT2_E_INVALID),
     ("vocab_padded", 70000, G.GPT2_E_INVALID),
     ("n_head", 8, G.GPT2_E_UNSUPPORTED),     # head_dim 8
-    ("batch", 300, G.GPT2_E_UNSUPPORTED),    # batch * seq_len > 16384
+    ("batch", 1100, G.GPT2_E_UNSUPPORTED),   # batch * seq_len > 65536
 ])
 def test_init_rejects_bad_config(lib, field, value, status):
     c = cfg_of("tiny", **{field: value})

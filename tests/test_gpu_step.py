@@ -1,8 +1,8 @@
 """Whole-step parity on the GPU, through the C ABI, against the float64 oracle.
 
-* fp32 path (tiny configuration and fp32 variants with a padded vocabulary, head_dim 32/64 and
-  ragged tiles): loss within 1e-5 relative, every gradient tensor within 1e-4 normwise relative
-  (max |g - g_ref| / max |g_ref|).
+* fp32 path (tiny configuration and fp32 variants with a padded vocabulary, head_dim 32/64,
+  ragged tiles and more rows than one token-sort chunk): loss within 1e-5 relative, every
+  gradient tensor within 1e-4 normwise relative (max |g - g_ref| / max |g_ref|).
 * bf16 path at the geometry of each large configuration with a batch the oracle finishes in
   seconds: loss within 1e-2 relative, per-tensor gradient cosine >= 0.999.
 * bf16 path at the full sizes, in the launch configuration the benchmark times: per-position
@@ -30,6 +30,8 @@ FP32_CASES = {
     "tiny_padded_vocab": (2, 64, 4, 64, 500, 512, 2, "fp32", "uniform"),
     "fp32_hd64_ragged": (1, 128, 2, 200, 300, 304, 2, "fp32", "uniform"),
     "fp32_hd32": (2, 96, 3, 72, 1000, 1024, 3, "fp32", "uniform"),
+    # 36864 rows: three token-sort chunks of up to 16384 positions, the last one partial
+    "fp32_rows_3_sort_chunks": (1, 64, 1, 1024, 500, 512, 36, "fp32", "zipf"),
 }
 BF16_REDUCED = {
     "gpt2_124m_T200": (12, 768, 12, 200, 50257, 50304, 1, "bf16", "zipf"),
@@ -37,6 +39,8 @@ BF16_REDUCED = {
     "gpt2_1p5b_T40": (48, 1600, 25, 40, 50257, 50304, 1, "bf16", "zipf"),
     "gpt2_124m_T640": (12, 768, 12, 640, 50257, 50304, 1, "bf16", "zipf"),
     "bf16_small_B3": (2, 256, 4, 100, 4000, 4096, 3, "bf16", "zipf"),
+    # 20480 rows: two token-sort chunks
+    "bf16_rows_2_sort_chunks": (1, 128, 2, 1024, 1000, 1024, 20, "bf16", "zipf"),
 }
 
 
@@ -73,6 +77,19 @@ def test_bf16_step_matches_oracle(name):
     worst = min((cosine(got[n], ref[n]), n) for n in ref)
     assert worst[0] >= BF16_GRAD_COS, worst
     assert np.all(got["wte"].reshape(ocfg.vocab_padded, -1)[ocfg.vocab:] == 0.0)
+    model.close()
+
+
+def test_rows_beyond_one_sort_chunk_bitwise():
+    """More rows than one token-sort chunk: the embedding gradient adds the sort chunks one after
+    another, so two identical steps agree bitwise."""
+    torch = torch_cuda()
+    model, ocfg, kind = make(G, BF16_REDUCED["bf16_rows_2_sort_chunks"])
+    x, y = tokens(kind, ocfg, seed=23)
+    _, r1, g1 = gpu_forward_backward(torch, model, x, y)
+    _, r2, g2 = gpu_forward_backward(torch, model, x, y)
+    assert np.array_equal(r1, r2)
+    assert np.array_equal(g1, g2)
     model.close()
 
 

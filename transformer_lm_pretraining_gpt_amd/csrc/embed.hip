@@ -4,18 +4,23 @@
 // (built the nanoGPT way, "Criei GPT-2 do zero com uma RTX 4090", section "Ambiente"), so its
 // gradient is the LM head's dW plus the scatter of dh0 rows by token id:
 //   dwte[v] += sum over positions p with x_p = v of dh0[p],   dwpe[t] = sum over b of dh0[b, t].
-// Determinism without float atomics: the (token, position) pairs are sorted once per batch (one
-// workgroup, stable LSD radix sort in LDS); the sorted list is cut into fixed chunks of 64
-// entries; a token whose run lies inside one chunk is summed and added by that chunk alone, and a
-// run that crosses chunk borders is summed from per-chunk partials, in chunk order, by the chunk
-// where it starts. Every sum therefore has one fixed order.
+// Determinism without float atomics: the positions are cut into sort chunks of 16384; each sort
+// chunk's (token, position) pairs are sorted by one workgroup (stable LSD radix sort in LDS, all
+// sort chunks in one launch); each sorted list is cut into fixed chunks of 64 entries; a token
+// whose run lies inside one chunk is summed and added by that chunk alone, and a run that crosses
+// chunk borders is summed from per-chunk partials, in chunk order, by the chunk where it starts.
+// The sort chunks add into the token gradient one after another, in position order. Every sum
+// therefore has one fixed order.
+#include <algorithm>
+
 #include "common.h"
 #include "kernels.h"
 
 namespace {
 
 constexpr int SORT_THREADS = 1024;
-constexpr int SORT_EPT = 16;  // elements per thread: M <= 16384
+constexpr int SORT_EPT = 16;  // elements per thread
+constexpr int SORT_CHUNK = SORT_THREADS * SORT_EPT;  // positions per sort chunk (16-bit in a key)
 constexpr int CHUNK = 64;
 
 __global__ __launch_bounds__(256) void embed_fwd_kernel(int M, int T, int d, int V,
@@ -43,11 +48,16 @@ __global__ __launch_bounds__(256) void embed_fwd_kernel(int M, int T, int d, int
   }
 }
 
-// Stable sort of key = token << 16 | position by token (LSD, 4 bits per pass over bits 16..31).
-// The initial order is by position, so the result is ascending in (token, position).
-__global__ __launch_bounds__(SORT_THREADS) void token_sort_kernel(int M, int V,
+// Block c sorts the positions [c * SORT_CHUNK, min(M, (c + 1) * SORT_CHUNK)): stable sort of
+// key = token << 16 | position within the sort chunk, by token (LSD, 4 bits per pass over bits
+// 16..31). The initial order is by position, so the result is ascending in (token, position).
+__global__ __launch_bounds__(SORT_THREADS) void token_sort_kernel(int M_all, int V,
                                                                    const int32_t* __restrict__ tokens,
                                                                    uint32_t* __restrict__ keys) {
+  const int64_t base = (int64_t)blockIdx.x * SORT_CHUNK;
+  const int M = (int)min<int64_t>(SORT_CHUNK, M_all - base);
+  tokens += base;
+  keys += base;
   __shared__ uint32_t cnt[16 * SORT_THREADS];  // digit-major counters, scanned in place
   __shared__ uint32_t buf[SORT_EPT * SORT_THREADS];
   __shared__ uint32_t wsum[SORT_THREADS / 64];
@@ -259,23 +269,31 @@ hipError_t launch_embed_fwd(int B, int T, int d, int V, const int32_t* tokens, c
 
 hipError_t launch_token_sort(int M, int V, const int32_t* tokens, uint32_t* keys, hipStream_t s) {
   if (M == 0) return hipSuccess;
-  if (M > SORT_THREADS * SORT_EPT || V > 65536) return hipErrorInvalidValue;
-  hipLaunchKernelGGL(token_sort_kernel, dim3(1), dim3(SORT_THREADS), 0, s, M, V, tokens, keys);
+  if (V > 65536) return hipErrorInvalidValue;
+  const int nsort = (M + SORT_CHUNK - 1) / SORT_CHUNK;
+  hipLaunchKernelGGL(token_sort_kernel, dim3(nsort), dim3(SORT_THREADS), 0, s, M, V, tokens, keys);
   return hipGetLastError();
 }
 
-int embed_bwd_chunks(int M) { return (M + CHUNK - 1) / CHUNK; }
+// 64-entry chunks of one sort chunk (the partial buffer is reused by every sort chunk)
+int embed_bwd_chunks(int M) { return (std::min(M, SORT_CHUNK) + CHUNK - 1) / CHUNK; }
 
 hipError_t launch_embed_bwd(int B, int T, int d, const uint32_t* keys, const float* dh0,
                             float* dwte, float* dwpe, int accumulate, float* seg_part,
                             hipStream_t s) {
   const int M = B * T;
   if (M == 0) return hipSuccess;
-  const int nch = embed_bwd_chunks(M);
-  hipLaunchKernelGGL(embed_seg_kernel, dim3(nch), dim3(256), 0, s, M, d, keys, dh0, dwte,
-                     seg_part);
-  hipLaunchKernelGGL(embed_fixup_kernel, dim3(nch), dim3(256), 0, s, M, d, nch, keys, dwte,
-                     seg_part);
+  // one sort chunk after another on the stream: each adds into dwte after the previous one
+  for (int base = 0; base < M; base += SORT_CHUNK) {
+    const int Mc = std::min(SORT_CHUNK, M - base);
+    const int nch = (Mc + CHUNK - 1) / CHUNK;
+    const uint32_t* kc = keys + base;
+    const float* hc = dh0 + (int64_t)base * d;
+    hipLaunchKernelGGL(embed_seg_kernel, dim3(nch), dim3(256), 0, s, Mc, d, kc, hc, dwte,
+                       seg_part);
+    hipLaunchKernelGGL(embed_fixup_kernel, dim3(nch), dim3(256), 0, s, Mc, d, nch, kc, dwte,
+                       seg_part);
+  }
   const int64_t n = (int64_t)T * (d / 4);
   hipLaunchKernelGGL(embed_wpe_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, B, T, d,
                      dh0, dwpe, accumulate);

@@ -36,7 +36,7 @@ gpt2_status fail(gpt2_status s, const std::string& msg) {
 
 constexpr int LN_ROWS_PER_BLOCK = 16;
 constexpr int COLSUM_ROWS_PER_BLOCK = 16;
-constexpr int MAX_ROWS = 16384;
+constexpr int MAX_ROWS = 65536;
 constexpr int TIMING_CAP = 4096;
 
 // ------------------------------------------------------------------------------ geometry
@@ -81,7 +81,7 @@ bool supported(const gpt2_config* c, std::string& why) {
   if (c->d_model % 8) { why = "d_model must be a multiple of 8"; return false; }
   if (c->d_model > 2048) { why = "d_model must be <= 2048"; return false; }
   if (c->vocab_padded % 8) { why = "vocab_padded must be a multiple of 8"; return false; }
-  if ((int64_t)c->batch * c->seq_len > MAX_ROWS) { why = "batch * seq_len must be <= 16384"; return false; }
+  if ((int64_t)c->batch * c->seq_len > MAX_ROWS) { why = "batch * seq_len must be <= 65536"; return false; }
   if (c->precision == GPT2_FP32 && c->vocab_padded > 32768) {
     why = "fp32 precision supports vocab_padded <= 32768"; return false;
   }

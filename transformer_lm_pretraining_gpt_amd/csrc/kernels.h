@@ -114,12 +114,14 @@ hipError_t launch_loss_mean(int M, const float* row_loss, const int32_t* targets
 // ------------------------------------------------------------------------------ embedding
 hipError_t launch_embed_fwd(int B, int T, int d, int V, const int32_t* tokens, const float* wte,
                             const float* wpe, float* h0, int* err, hipStream_t s);
-// Stable sort of (token, position) pairs: keys[i] = token << 16 | position, ascending.
+// Stable sort of (token, position) pairs within each sort chunk of 16384 positions:
+// keys[c * 16384 + i] = token << 16 | (position - c * 16384), ascending within the chunk.
 hipError_t launch_token_sort(int M, int V, const int32_t* tokens, uint32_t* keys, hipStream_t s);
 // dwte[tok] += sum of dh0 rows with that token (deterministic); dwpe = (acc ? dwpe : 0) + sum_b.
 hipError_t launch_embed_bwd(int B, int T, int d, const uint32_t* keys, const float* dh0,
                             float* dwte, float* dwpe, int accumulate, float* seg_part,
                             hipStream_t s);
+// 64-entry chunks of the largest sort chunk: seg_part holds 2 * embed_bwd_chunks(M) * d floats.
 int embed_bwd_chunks(int M);
 
 // ------------------------------------------------------------------------------ optimizer
