@@ -32,7 +32,7 @@ sys.path.insert(0, ROOT)
 
 PAGES_TOKENS_PER_S = 120_000.0  # GPT-2 124M on one RTX 4090 (context only)
 HBM_PEAK_GBS = 8000.0
-OTHER_WORKLOADS = ("gpt2_350m", "gpt2_1p5b", "gpt2_124m_t8192")
+OTHER_WORKLOADS = ("gpt2_350m", "gpt2_1p5b", "gpt2_124m_t8192", "gpt2_124m_mb32")
 
 # families timed per launch by the library: (name, unit of its work figure, roofline)
 FAMILIES = (

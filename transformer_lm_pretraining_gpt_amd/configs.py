@@ -1,4 +1,5 @@
-"""The five named workloads of the step and the FLOP accounting used for MFU.
+"""The five named workloads of the step (and the 124M model at micro-batch 32) and the FLOP
+accounting used for MFU.
 
 Geometry of GPT-2 small/medium/XL; micro-batch and sequence length per workload. The 124M
 workload is the one the pages train ("Criei GPT-2 do zero com uma RTX 4090", section
@@ -14,6 +15,9 @@ PRESETS = {
     "gpt2_350m": (24, 1024, 16, 1024, 50257, 50304, 8, "bf16", "zipf"),
     "gpt2_1p5b": (48, 1600, 25, 1024, 50257, 50304, 4, "bf16", "zipf"),
     "gpt2_124m_t8192": (12, 768, 12, 8192, 50257, 50304, 2, "bf16", "zipf"),
+    # not one of the five: the 124M model at twice the micro-batch (32768 rows per step), which
+    # one GPU's HBM holds with room to spare
+    "gpt2_124m_mb32": (12, 768, 12, 1024, 50257, 50304, 32, "bf16", "zipf"),
 }
 
 # MI355X dense bf16 matrix peak: 256 CUs x 2.4 GHz x 4096 FLOP/clock/CU
