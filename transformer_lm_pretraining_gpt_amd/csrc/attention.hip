@@ -802,12 +802,17 @@ __global__ __launch_bounds__(THREADS, 2) void attn_bwd_dkdv64_kernel(
   store_head_row<bf16, 64>(dv, dK + dm, ld, kj, T_, 1.0f, h, l32);
 }
 
-// dQ for 256 queries per block (wave w: query groups w and 7 - w, one query per lane):
-// S^T = K Q^T and dP^T = V dO^T with the query's Q and dO rows as register B operands, then
-// dQ^T += K^T dS^T from the transposed K tile. Key tiles stream through a three-stage LDS ring.
-// Each query's D = dO . O is computed here from its own rows and written with lse log2 e as the
-// pair the dK/dV kernel (launched after this one) reads.
-__global__ __launch_bounds__(THREADS, 2) void attn_bwd_dq64_kernel(
+// dQ for 128 queries per block (wave w: the 32-query group w, one query per lane): S^T = K Q^T
+// and dP^T = V dO^T with the query's Q and dO rows as register B operands, then dQ^T += K^T dS^T
+// from the transposed K tile. Key tiles stream through a three-stage LDS ring. One group per wave
+// keeps a wave at about 130 registers, so three blocks (48 KB of LDS each) share a CU; two groups
+// per wave (256 queries per block) needed about 200 registers and ran two waves per SIMD, about 8 %
+// slower over the whole attention backward at the GPT-2 124M shape. Each query's D = dO . O is
+// computed here from its own rows and written with lse log2 e as the pair the dK/dV kernel
+// (launched after this one) reads.
+constexpr int DQ64_Q = 128;  // queries per block
+
+__global__ __launch_bounds__(THREADS, 3) void attn_bwd_dq64_kernel(
     const bf16* __restrict__ qkv, const bf16* __restrict__ out, const bf16* __restrict__ dout,
     const float* __restrict__ lse, float2* __restrict__ lsed, bf16* __restrict__ dqkv, int T_,
     int H) {
@@ -816,7 +821,7 @@ __global__ __launch_bounds__(THREADS, 2) void attn_bwd_dq64_kernel(
   __shared__ __attribute__((aligned(1024))) char smem[NST * 16384];
   const int tid = threadIdx.x, lane = tid & 63, h = lane >> 5, l32 = lane & 31;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int nqb = (T_ + F64_Q - 1) / F64_Q;
+  const int nqb = (T_ + DQ64_Q - 1) / DQ64_Q;
   const int qb = nqb - 1 - (int)blockIdx.y;  // heaviest query blocks dispatched first
   const int bh = blockIdx.x, b = bh / H, hh = bh % H;
   const int dm = H * 64;
@@ -826,20 +831,16 @@ __global__ __launch_bounds__(THREADS, 2) void attn_bwd_dq64_kernel(
   const bf16* V = Q + 2 * dm;
   const bf16* dO = dout + (int64_t)b * T_ * dm + hh * 64;
   const bf16* O = out + (int64_t)b * T_ * dm + hh * 64;
-  const int q0 = qb * F64_Q;
-  const int ntiles = min(T_, q0 + F64_Q) / 64;
+  const int q0 = qb * DQ64_Q;
+  const int ntiles = min(T_, q0 + DQ64_Q) / 64;
 
-  int qg[2];
-  qg[0] = q0 + 32 * wave;
-  qg[1] = q0 + 32 * (7 - wave);
-  u32x4 qf[2][4], df[2][4];
-  float lse2[2], dsum[2];
-  f32x16 dq[2][2];
-#pragma unroll
-  for (int i = 0; i < 2; ++i) {
-    const int qi = qg[i] + l32;
-    load_row_frags<bf16, 64>(qf[i], Q, ld, qi, T_, h);
-    load_row_frags<bf16, 64>(df[i], dO, dm, qi, T_, h);
+  const int qg = q0 + 32 * wave;  // this wave's first query
+  const int qi = qg + l32;        // this lane's query
+  u32x4 qf[4], df[4];
+  load_row_frags<bf16, 64>(qf, Q, ld, qi, T_, h);
+  load_row_frags<bf16, 64>(df, dO, dm, qi, T_, h);
+  float dsum;
+  {
     // D = dO . O over the head's 64 columns: this lane holds 32 of them (half h), the lane 32
     // apart the other 32
     u32x4 of[4];
@@ -849,16 +850,17 @@ __global__ __launch_bounds__(THREADS, 2) void attn_bwd_dq64_kernel(
     for (int s = 0; s < 4; ++s) {
       float a[8], g[8];
       Vec<bf16>::unpack(of[s], a);
-      Vec<bf16>::unpack(df[i][s], g);
+      Vec<bf16>::unpack(df[s], g);
 #pragma unroll
       for (int e = 0; e < 8; ++e) part = fmaf(a[e], g[e], part);
     }
-    dsum[i] = part + __shfl_xor(part, 32, 64);
-    lse2[i] = qi < T_ ? lse[(int64_t)bh * T_ + qi] * LOG2E : 0.0f;
-    // the {lse log2 e, D} pairs the dK/dV kernel streams with its query tiles
-    if (h == 0 && qi < T_) lsed[(int64_t)bh * T_ + qi] = make_float2(lse2[i], dsum[i]);
-    dq[i][0] = dq[i][1] = f32x16{};
+    dsum = part + __shfl_xor(part, 32, 64);
   }
+  const float lse2 = qi < T_ ? lse[(int64_t)bh * T_ + qi] * LOG2E : 0.0f;
+  // the {lse log2 e, D} pairs the dK/dV kernel streams with its query tiles
+  if (h == 0 && qi < T_) lsed[(int64_t)bh * T_ + qi] = make_float2(lse2, dsum);
+  f32x16 dq[2];
+  dq[0] = dq[1] = f32x16{};
   const float c = LOG2E / 8.0f;
 
   uint32_t off[2];
@@ -872,7 +874,7 @@ __global__ __launch_bounds__(THREADS, 2) void attn_bwd_dq64_kernel(
   for (int t = 0; t < NST - 1; ++t)
     if (t < ntiles) issue(t);
 
-// the tile loop is unrolled over the three stages so that each stage's LDS offset is a
+  // the tile loop is unrolled over the three stages so that each stage's LDS offset is a
   // compile-time constant (folded into the LDS instructions' offsets)
   auto tile = [&](auto stc, int kt) {
     constexpr int ST = decltype(stc)::value;
@@ -882,66 +884,60 @@ __global__ __launch_bounds__(THREADS, 2) void attn_bwd_dq64_kernel(
     const char* ktile = smem + ST * 16384;
     const char* vtile = ktile + 8192;
     const int key0 = kt * 64;
+    if (key0 > qg + 31 || qg >= T_) return;  // every key of the tile is after the group
+    // one 32-key sub-tile in three steps: S^T and dP^T, then dS^T, then dQ^T
+    auto scores = [&](int js, f32x16& sacc, f32x16& dpacc) {
+      sacc = f32x16{};
+      dpacc = f32x16{};
 #pragma unroll
-    for (int i = 0; i < 2; ++i) {
-      if (key0 > qg[i] + 31 || qg[i] >= T_) continue;  // every key of the tile is after the group
-      const int qi = qg[i] + l32;
-      // one 32-key sub-tile in three steps: S^T and dP^T, then dS^T, then dQ^T
-      auto scores = [&](int js, f32x16& sacc, f32x16& dpacc) {
-        sacc = f32x16{};
-        dpacc = f32x16{};
+      for (int s = 0; s < 4; ++s) {
+        Mfma<bf16>::mma(sacc, HeadTile::frag(ktile, js * 32, s, lane), qf[s]);
+        Mfma<bf16>::mma(dpacc, HeadTile::frag(vtile, js * 32, s, lane), df[s]);
+      }
+    };
+    auto dscores = [&](int js, bool diag, const f32x16& sacc, const f32x16& dpacc,
+                       u32x4 (&dsb)[2]) {
+      float ds[16];
 #pragma unroll
-        for (int s = 0; s < 4; ++s) {
-          Mfma<bf16>::mma(sacc, HeadTile::frag(ktile, js * 32, s, lane), qf[i][s]);
-          Mfma<bf16>::mma(dpacc, HeadTile::frag(vtile, js * 32, s, lane), df[i][s]);
-        }
-      };
-      auto dscores = [&](int js, bool diag, const f32x16& sacc, const f32x16& dpacc,
-                         u32x4 (&dsb)[2]) {
-        float ds[16];
+      for (int r = 0; r < 16; ++r)
+        ds[r] = fast_exp2(fmaf(sacc[r], c, -lse2)) * (dpacc[r] - dsum);
+      if (diag) {  // keys after the query: zero (a branch of its own, taken on diagonal tiles)
+        const int j0 = key0 + js * 32;
 #pragma unroll
         for (int r = 0; r < 16; ++r)
-          ds[r] = fast_exp2(fmaf(sacc[r], c, -lse2[i])) * (dpacc[r] - dsum[i]);
-        if (diag) {  // keys after the query: zero (a branch of its own, taken on diagonal tiles)
-          const int j0 = key0 + js * 32;
-#pragma unroll
-          for (int r = 0; r < 16; ++r)
-            if (j0 + mfma_row(r, h) > qi) ds[r] = 0.0f;
-        }
-#pragma unroll
-        for (int u = 0; u < 2; ++u) dsb[u] = pack8(ds + 8 * u);
-      };
-      auto accumulate = [&](int js, const u32x4 (&dsb)[2]) {
-#pragma unroll
-        for (int u = 0; u < 2; ++u)
-#pragma unroll
-          for (int db = 0; db < 2; ++db)
-            Mfma<bf16>::mma(dq[i][db], HeadTile::tfrag(ktile, db * 32, js * 32 + 16 * u, lane), dsb[u]);
-      };
-      // The two 32-key sub-tiles one after the other: keeping both sub-tiles' scores live (so
-      // one's MFMAs overlap the other's exponentials) needs more registers than the 256 a wave
-      // has at two blocks per CU, and the spill reloads' vmcnt waits drained the K/V prefetch.
-#pragma unroll
-      for (int js = 0; js < 2; ++js) {
-        const int j0 = key0 + js * 32;
-        if (j0 > qg[i] + 31) continue;
-        f32x16 sacc, dpacc;
-        u32x4 dsb[2];
-        scores(js, sacc, dpacc);
-        dscores(js, j0 + 31 > qg[i], sacc, dpacc, dsb);
-        accumulate(js, dsb);
+          if (j0 + mfma_row(r, h) > qi) ds[r] = 0.0f;
       }
-    }
+#pragma unroll
+      for (int u = 0; u < 2; ++u) dsb[u] = pack8(ds + 8 * u);
     };
+    auto accumulate = [&](int js, const u32x4 (&dsb)[2]) {
+#pragma unroll
+      for (int u = 0; u < 2; ++u)
+#pragma unroll
+        for (int db = 0; db < 2; ++db)
+          Mfma<bf16>::mma(dq[db], HeadTile::tfrag(ktile, db * 32, js * 32 + 16 * u, lane), dsb[u]);
+    };
+    // The two 32-key sub-tiles one after the other: keeping both sub-tiles' scores live (so one's
+    // MFMAs overlap the other's exponentials) takes the wave to about 210 registers, two waves per
+    // SIMD instead of three (or spills at three).
+#pragma unroll
+    for (int js = 0; js < 2; ++js) {
+      const int j0 = key0 + js * 32;
+      if (j0 > qg + 31) continue;
+      f32x16 sacc, dpacc;
+      u32x4 dsb[2];
+      scores(js, sacc, dpacc);
+      dscores(js, j0 + 31 > qg, sacc, dpacc, dsb);
+      accumulate(js, dsb);
+    }
+  };
   for (int kt0 = 0; kt0 < ntiles; kt0 += 3) {
     tile(std::integral_constant<int, 0>{}, kt0);
     if (kt0 + 1 < ntiles) tile(std::integral_constant<int, 1>{}, kt0 + 1);
     if (kt0 + 2 < ntiles) tile(std::integral_constant<int, 2>{}, kt0 + 2);
   }
-#pragma unroll
-  for (int i = 0; i < 2; ++i)
-    store_head_row<bf16, 64>(dq[i], dqkv + (int64_t)b * T_ * ld + hh * 64, ld, qg[i] + l32, T_,
-                             1.0f / 8.0f, h, l32);
+  store_head_row<bf16, 64>(dq, dqkv + (int64_t)b * T_ * ld + hh * 64, ld, qi, T_, 1.0f / 8.0f, h,
+                           l32);
 }
 
 // Grids are (batch * heads, blocks along the sequence) with the heaviest causal blocks at y = 0.
@@ -973,7 +969,7 @@ hipError_t bwd_t(int B, int T_, int H, const void* qkv, const void* out, const f
     if (T_ % 64 == 0) {
       // dQ first: it also writes the {lse log2 e, D} pairs that dK/dV read
       float2* lsed = reinterpret_cast<float2*>(dsum);
-      hipLaunchKernelGGL(attn_bwd_dq64_kernel, dim3(B * H, (T_ + F64_Q - 1) / F64_Q), dim3(THREADS),
+      hipLaunchKernelGGL(attn_bwd_dq64_kernel, dim3(B * H, (T_ + DQ64_Q - 1) / DQ64_Q), dim3(THREADS),
                          0, s, static_cast<const bf16*>(qkv), static_cast<const bf16*>(out),
                          static_cast<const bf16*>(dout), lse, lsed, static_cast<bf16*>(dqkv), T_,
                          H);
