@@ -242,7 +242,7 @@ def main():
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle's cpu_baseline leg")
     ap.add_argument("--no-breakdown", action="store_true", help="skip per-family kernel timing")
     ap.add_argument("--no-variants", action="store_true",
-                    help="skip the masked-target and 32x gradient-accumulation variants")
+                    help="skip the forward+backward-only, masked-target and 32x gradient-accumulation variants")
     ap.add_argument("--no-configs", action="store_true",
                     help="skip the 350M, 1.5B and T=8192 workloads")
     ap.add_argument("--config-steps", type=int, default=20)
@@ -381,7 +381,9 @@ def main():
 
 
 def variants(W, torch):
-    """Two variants of the timed step on the same windows:
+    """Three variants of the timed step on the same windows:
+    * forward_backward_only: forward_loss + backward without the AdamW step (the optimizer's
+      share of the step is the difference to the headline);
     * sft_masked_targets: targets of synthetic prompt spans set to -1 (not trained), the rest as
       in the headline step; tokens/s counts every position processed;
     * grad_accum_32: one AdamW step per 32 micro-batches (forward + backward with accumulate = 1
@@ -411,6 +413,17 @@ def variants(W, torch):
         model.forward_loss(W.xs[i], yms[i], loss)
         model.backward(1.0, False)
         model.adamw_step(6e-4, 0.9, 0.95, 1e-8, 0.1)
+
+    def fwd_bwd(r):
+        i = first + r % (n - first)
+        model.forward_loss(W.xs[i], W.ys[i], loss)
+        model.backward(1.0, False)
+
+    fwd_bwd(0)
+    ms = timed(fwd_bwd, 20)
+    model.check()
+    res["forward_backward_only"] = {"ms_per_step": round(ms, 3),
+                                    "tokens_per_s": round(M / (ms / 1e3), 1)}
 
     masked(0)
     ms = timed(masked, 10)
