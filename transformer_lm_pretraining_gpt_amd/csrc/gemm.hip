@@ -997,6 +997,32 @@ __global__ void splitk_reduce4_kernel(const float* __restrict__ part, int splits
   *out = alpha * s + prev;
 }
 
+// Split-K partials (dense (M, N) per split) summed in split order, scaled by alpha times
+// *alpha_scale (when given) and rounded to bf16 into C; four columns per thread.
+__global__ void splitk_reduce_bf16_kernel(const float* __restrict__ part, int splits,
+                                          int64_t stride, int M, int N, bf16* __restrict__ C,
+                                          int64_t ldc, float alpha,
+                                          const float* __restrict__ alpha_scale) {
+  const int nv = N / 4;
+  const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (idx >= (int64_t)M * nv) return;
+  const int row = (int)(idx / nv), c4 = (int)(idx % nv);
+  const int64_t src = (int64_t)row * N + 4 * c4;
+  f32x4 s = f32x4{0, 0, 0, 0};
+  int z = 0;
+  for (; z + 4 <= splits; z += 4) {  // four loads in flight, still added in split order
+    const f32x4 a = *reinterpret_cast<const f32x4*>(part + (int64_t)z * stride + src);
+    const f32x4 b = *reinterpret_cast<const f32x4*>(part + (int64_t)(z + 1) * stride + src);
+    const f32x4 c = *reinterpret_cast<const f32x4*>(part + (int64_t)(z + 2) * stride + src);
+    const f32x4 d = *reinterpret_cast<const f32x4*>(part + (int64_t)(z + 3) * stride + src);
+    s = (((s + a) + b) + c) + d;
+  }
+  for (; z < splits; ++z) s += *reinterpret_cast<const f32x4*>(part + (int64_t)z * stride + src);
+  const float a = alpha_scale ? alpha * *alpha_scale : alpha;
+  const f32x4 v = a * s;
+  st8(C + (int64_t)row * ldc + 4 * c4, u32x2{pack_bf16(v[0], v[1]), pack_bf16(v[2], v[3])});
+}
+
 // Blocks of `kernel` (nt threads each) resident at once on the current device.
 template <typename K>
 int resident_blocks(K kernel, int nt) {
@@ -1122,6 +1148,18 @@ hipError_t launch_gemm(bool is_bf16, int a_kmajor, int b_kmajor, int tile, int s
   if (p.M <= 0 || p.N <= 0) return hipSuccess;
   return is_bf16 ? launch_type<bf16>(a_kmajor, b_kmajor, tile, splits, tag, p, s)
                  : launch_type<float>(a_kmajor, b_kmajor, tile, splits, tag, p, s);
+}
+
+hipError_t launch_splitk_reduce_bf16(const float* part, int splits, int64_t split_stride, int M,
+                                     int N, void* C, int64_t ldc, float alpha,
+                                     const float* alpha_scale, hipStream_t s) {
+  if (N % 4 || ldc % 4 || split_stride % 4) return hipErrorInvalidValue;
+  const int64_t n4 = (int64_t)M * (N / 4);
+  if (n4 == 0) return hipSuccess;
+  hipLaunchKernelGGL(splitk_reduce_bf16_kernel, dim3((unsigned)((n4 + 255) / 256)), dim3(256), 0, s,
+                     part, splits, split_stride, M, N, static_cast<bf16*>(C), ldc, alpha,
+                     alpha_scale);
+  return hipGetLastError();
 }
 
 hipError_t launch_splitk_reduce(const float* part, int splits, int64_t split_stride, int M, int N,

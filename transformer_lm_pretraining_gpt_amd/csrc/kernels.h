@@ -52,6 +52,11 @@ int gemm_pick_tile(int M, int N);
 // Sum split-K partials: C[m, n] = alpha * sum_z part[z][m, n] + beta * C[m, n] (fixed z order).
 hipError_t launch_splitk_reduce(const float* part, int splits, int64_t split_stride, int M, int N,
                                 float* C, int64_t ldc, float alpha, float beta, hipStream_t s);
+// The same into a bf16 C from dense (M, N) partials, scaled by alpha * *alpha_scale (when given):
+// C[m, n] = bf16(alpha * sum_z part[z][m, n]). N, ldc and split_stride multiples of 4.
+hipError_t launch_splitk_reduce_bf16(const float* part, int splits, int64_t split_stride, int M,
+                                     int N, void* C, int64_t ldc, float alpha,
+                                     const float* alpha_scale, hipStream_t s);
 
 // ------------------------------------------------------------------------------ attention
 // qkv: (B*T, 3*d); out: (B*T, d); lse: (B, H, T) fp32.
