@@ -41,6 +41,9 @@ BF16_REDUCED = {
     "bf16_small_B3": (2, 256, 4, 100, 4000, 4096, 3, "bf16", "zipf"),
     # 20480 rows: two token-sort chunks
     "bf16_rows_2_sort_chunks": (1, 128, 2, 1024, 1000, 1024, 20, "bf16", "zipf"),
+    # padded vocabulary not a multiple of 64: the LM-head products take the register-staged GEMM
+    # (K = Vp for the input gradient, no K-splits) and a ragged last row tile of the dW
+    "bf16_vocab_1000": (2, 128, 2, 96, 990, 1000, 2, "bf16", "zipf"),
 }
 
 
