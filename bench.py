@@ -251,7 +251,7 @@ def main():
                          "the reference dispatch that scales HBM byte counters")
     args = ap.parse_args()
     if args.gpus != 1:
-        print(json.dumps({"error": "this build runs on exactly one GPU; --gpus must be 1",
+        print(json.dumps({"error": "the benchmark runs the step on exactly one GPU; --gpus must be 1",
                           "n_gpus": args.gpus}))
         sys.exit(2)
 
