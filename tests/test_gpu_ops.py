@@ -199,7 +199,8 @@ def test_attention_fp32(hd, T):
 
 
 # T a multiple of 64 with head_dim 64 takes the pipelined path: one 64-key tile (T=64), a last
-# 256-query block holding only 64 queries (T=320), and two full blocks (T=1024); the others take
+# block holding only 64 queries (T=320: the forward's 256-query and the dQ kernel's 128-query
+# blocks, whose waves past the end only load and wait), and full blocks (T=1024); the others take
 # the general path.
 @pytest.mark.parametrize("hd,T,H", [(64, 200, 3), (64, 64, 3), (64, 320, 2), (64, 1024, 2),
                                     (32, 136, 2), (16, 72, 4)])
