@@ -261,15 +261,17 @@ __global__ __launch_bounds__(THREADS) void attn_fwd_kernel(const T* __restrict__
 
 // ------------------------------------------------------- forward, bf16 with head_dim 64
 // Path for bf16 heads of 64 when T is a multiple of 64. K and V tiles of 64 keys go straight
-// from memory into a three-stage LDS ring; the K tile is read as K-major A fragments of S^T =
+// from memory into a two-stage LDS ring; the K tile is read as K-major A fragments of S^T =
 // K Q^T, and the V tile, stored as it is ([key][d] rows), is read transposed with
 // ds_read_b64_tr_b16 as the A operand of O^T = V^T P^T, in the key order that the probability
-// registers already have. A block owns 256 queries; wave w owns the 32-query groups w and 7 - w,
-// so the four waves see about the same number of keys under the causal mask. Only the diagonal
-// tile of a group is masked, and the running output is rescaled only when some lane's maximum
-// grew (alpha = 1 otherwise, so skipping it changes nothing).
-constexpr int F64_Q = 256;        // queries per block
-constexpr int F64_NST = 3;        // LDS stages
+// registers already have. A block owns 128 queries, wave w the 32-query group w: a wave needs
+// about 110 registers and a block 32 KB of LDS, so four blocks (four waves per SIMD) share a CU.
+// Two groups per wave (256 queries per block, groups w and 7 - w) with a three-stage ring ran
+// three waves per SIMD and was 12-14 % slower at T = 1024 and 8192. Only the diagonal tile of a
+// group is masked, and the running output is rescaled only when some lane's maximum grew
+// (alpha = 1 otherwise, so skipping it changes nothing).
+constexpr int F64_Q = 128;        // queries per block
+constexpr int F64_NST = 2;        // LDS stages
 constexpr int F64_STAGE = 16384;  // K tile (8 KB) then V tile (8 KB)
 
 // A operand V^T[d0 + l%32][keys key0 + 4h + 0..3, key0 + 8 + 4h + 0..3] (h = l / 32) from a V
@@ -311,20 +313,13 @@ __global__ __launch_bounds__(THREADS, 3) void attn_fwd64_kernel(const bf16* __re
   const int q0 = qb * F64_Q;
   const int ntiles = min(T_, q0 + F64_Q) / 64;
 
-  int qg[2];
-  qg[0] = q0 + 32 * wave;
-  qg[1] = q0 + 32 * (7 - wave);
-  u32x4 qf[2][4];
-#pragma unroll
-  for (int i = 0; i < 2; ++i) load_row_frags<bf16, 64>(qf[i], Q, ld, qg[i] + l32, T_, h);
-  f32x16 o[2][2];
-  float m_run[2], l_run[2];
-#pragma unroll
-  for (int i = 0; i < 2; ++i) {
-    o[i][0] = o[i][1] = f32x16{};
-    m_run[i] = -INFINITY;
-    l_run[i] = 0.0f;
-  }
+  const int qg = q0 + 32 * wave;  // this wave's first query
+  const int qi = qg + l32;        // this lane's query
+  u32x4 qf[4];
+  load_row_frags<bf16, 64>(qf, Q, ld, qi, T_, h);
+  f32x16 o[2];
+  o[0] = o[1] = f32x16{};
+  float m_run = -INFINITY, l_run = 0.0f;
   const float c = LOG2E / 8.0f;  // log2(e) / sqrt(64)
 
   uint32_t offk[TK::PER_WAVE], offv[TV::PER_WAVE];
@@ -343,7 +338,7 @@ __global__ __launch_bounds__(THREADS, 3) void attn_fwd64_kernel(const bf16* __re
   for (int s = 0; s < F64_NST - 1; ++s)
     if (s < ntiles) issue(s);
 
-// the tile loop is unrolled over the three stages so that each stage's LDS offset is a
+  // the tile loop is unrolled over the two stages so that each stage's LDS offset is a
   // compile-time constant (folded into the LDS instructions' offsets)
   auto tile = [&](auto stc, int kt) {
     constexpr int ST = decltype(stc)::value;
@@ -353,18 +348,18 @@ __global__ __launch_bounds__(THREADS, 3) void attn_fwd64_kernel(const bf16* __re
     const char* ktile = smem + ST * F64_STAGE;
     const char* vtile = ktile + 8192;
     const int key0 = kt * 64;
-    // one query group in three steps: S^T, then the online softmax (P^T packed to bf16), then
+    if (key0 > qg + 31 || qg >= T_) return;  // every key of the tile is after the group
+    // the group in three steps: S^T, then the online softmax (P^T packed to bf16), then
     // O^T += V^T P^T
-    auto scores = [&](int i, f32x16 (&sacc)[2]) {
+    auto scores = [&](f32x16 (&sacc)[2]) {
 #pragma unroll
       for (int js = 0; js < 2; ++js) {
         sacc[js] = f32x16{};
 #pragma unroll
-        for (int s = 0; s < 4; ++s) Mfma<bf16>::mma(sacc[js], TK::frag(ktile, js * 32, s, lane), qf[i][s]);
+        for (int s = 0; s < 4; ++s) Mfma<bf16>::mma(sacc[js], TK::frag(ktile, js * 32, s, lane), qf[s]);
       }
     };
-    auto softmax = [&](int i, bool diag, f32x16 (&sacc)[2], u32x4 (&pb)[2][2]) {
-      const int qi = qg[i] + l32;
+    auto softmax = [&](bool diag, f32x16 (&sacc)[2], u32x4 (&pb)[2][2]) {
       float mloc = -INFINITY;
       if (diag) {
 #pragma unroll
@@ -383,15 +378,15 @@ __global__ __launch_bounds__(THREADS, 3) void attn_fwd64_kernel(const bf16* __re
       // The running maximum moves only when some row's maximum grew by more than 2^8: below
       // that, exp2 of the scores minus the older maximum stays below 256 (no overflow; bf16
       // keeps its relative precision), and the normalisation by the row sum is unchanged.
-      if (__builtin_amdgcn_ballot_w64(mloc > m_run[i] + 8.0f) != 0) {
-        const float m_new = fmaxf(m_run[i], mloc);
-        const float alpha = fast_exp2(m_run[i] - m_new);
-        o[i][0] *= alpha;
-        o[i][1] *= alpha;
-        l_run[i] *= alpha;
-        m_run[i] = m_new;
+      if (__builtin_amdgcn_ballot_w64(mloc > m_run + 8.0f) != 0) {
+        const float m_new = fmaxf(m_run, mloc);
+        const float alpha = fast_exp2(m_run - m_new);
+        o[0] *= alpha;
+        o[1] *= alpha;
+        l_run *= alpha;
+        m_run = m_new;
       }
-      const float m_use = m_run[i];
+      const float m_use = m_run;
       float lsum = 0.0f;
 #pragma unroll
       for (int js = 0; js < 2; ++js) {
@@ -406,39 +401,30 @@ __global__ __launch_bounds__(THREADS, 3) void attn_fwd64_kernel(const bf16* __re
           pb[js][u] = u32x4{pack_bf16(p[8 * u], p[8 * u + 1]), pack_bf16(p[8 * u + 2], p[8 * u + 3]),
                             pack_bf16(p[8 * u + 4], p[8 * u + 5]), pack_bf16(p[8 * u + 6], p[8 * u + 7])};
       }
-      l_run[i] += lsum;
+      l_run += lsum;
     };
-    auto pv = [&](int i, const u32x4 (&pb)[2][2]) {
+    auto pv = [&](const u32x4 (&pb)[2][2]) {
 #pragma unroll
       for (int js = 0; js < 2; ++js)
 #pragma unroll
         for (int u = 0; u < 2; ++u)
 #pragma unroll
           for (int db = 0; db < 2; ++db)
-            Mfma<bf16>::mma(o[i][db], vt_frag(vtile, db * 32, js * 32 + 16 * u, lane), pb[js][u]);
+            Mfma<bf16>::mma(o[db], vt_frag(vtile, db * 32, js * 32 + 16 * u, lane), pb[js][u]);
     };
-#pragma unroll
-    for (int i = 0; i < 2; ++i) {
-      if (key0 > qg[i] + 31 || qg[i] >= T_) continue;  // every key of the tile is after the group
-      f32x16 sacc[2];
-      u32x4 pb[2][2];
-      scores(i, sacc);
-      softmax(i, key0 + 63 > qg[i], sacc, pb);
-      pv(i, pb);
-    }
-    };
-  for (int kt0 = 0; kt0 < ntiles; kt0 += 3) {
+    f32x16 sacc[2];
+    u32x4 pb[2][2];
+    scores(sacc);
+    softmax(key0 + 63 > qg, sacc, pb);
+    pv(pb);
+  };
+  for (int kt0 = 0; kt0 < ntiles; kt0 += 2) {
     tile(std::integral_constant<int, 0>{}, kt0);
     if (kt0 + 1 < ntiles) tile(std::integral_constant<int, 1>{}, kt0 + 1);
-    if (kt0 + 2 < ntiles) tile(std::integral_constant<int, 2>{}, kt0 + 2);
   }
-#pragma unroll
-  for (int i = 0; i < 2; ++i) {
-    const int qi = qg[i] + l32;
-    const float l_tot = l_run[i] + __shfl_xor(l_run[i], 32, 64);
-    store_head_row<bf16, 64>(o[i], out + (int64_t)b * T_ * dm + hh * 64, dm, qi, T_, 1.0f / l_tot, h, l32);
-    if (h == 0 && qi < T_) lse[(int64_t)bh * T_ + qi] = (m_run[i] + log2f(l_tot)) * LN2;
-  }
+  const float l_tot = l_run + __shfl_xor(l_run, 32, 64);
+  store_head_row<bf16, 64>(o, out + (int64_t)b * T_ * dm + hh * 64, dm, qi, T_, 1.0f / l_tot, h, l32);
+  if (h == 0 && qi < T_) lse[(int64_t)bh * T_ + qi] = (m_run + log2f(l_tot)) * LN2;
 }
 
 // --------------------------------------------------------------------- backward: D = rowsum
