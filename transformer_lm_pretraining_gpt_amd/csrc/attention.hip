@@ -649,12 +649,13 @@ DEV u32x4 pack8(const float* p) {
 // dK and dV for 128 keys per block (32 per wave, one key per lane): S = Q K^T and dP = dO V^T
 // with the key's K and V rows as register B operands, then dV^T += dO^T P and dK^T += Q^T dS from
 // the transposed tiles. Query tiles of 64 stream through a three-stage LDS ring with their
-// {lse log2 e, D} pairs.
+// lse log2 e and -D values; dP's accumulators start from -D, so the MFMAs leave dP - D and
+// dS = P (dP - D) takes one multiply per element.
 constexpr int B64_KEYS = 128;
-constexpr int B64_STAGE = 8192 + 8192 + 512;  // Q tile, dO tile, 64 x float2
+constexpr int B64_STAGE = 8192 + 8192 + 512;  // Q tile, dO tile, 64 lse log2 e and 64 -D
 
 __global__ __launch_bounds__(THREADS, 2) void attn_bwd_dkdv64_kernel(
-    const bf16* __restrict__ qkv, const bf16* __restrict__ dout, const float2* __restrict__ lsed,
+    const bf16* __restrict__ qkv, const bf16* __restrict__ dout, const float* __restrict__ lsd,
     bf16* __restrict__ dqkv, int T_, int H) {
   constexpr int NST = 3;
   constexpr int LW = 2 * HeadTile::PER_WAVE + 1;
@@ -668,7 +669,9 @@ __global__ __launch_bounds__(THREADS, 2) void attn_bwd_dkdv64_kernel(
   const bf16* K = Q + dm;
   const bf16* V = Q + 2 * dm;
   const bf16* dO = dout + (int64_t)b * T_ * dm + hh * 64;
-  const float2* lsed_bh = lsed + (int64_t)bh * T_;
+  const float* lsd_bh = lsd + (int64_t)bh * T_;
+  // lanes 0..3 load four lse log2 e each, lanes 4..7 four -D from the second half of the buffer
+  const uint32_t lsd_off = lane < 4 ? 16u * lane : 4u * (uint32_t)gridDim.x * T_ + 16u * (lane - 4);
   const int k0 = blockIdx.y * B64_KEYS;  // key blocks near the start (most queries) go first
   const int kg = k0 + 32 * wave;         // this wave's first key
   const int kj = kg + l32;               // this lane's key
@@ -689,8 +692,8 @@ __global__ __launch_bounds__(THREADS, 2) void attn_bwd_dkdv64_kernel(
     const int q = (qt0 + t) * 64;
     HeadTile::issue(buffer_at(Q + (int64_t)q * ld), offq, st, wave);
     HeadTile::issue(buffer_at(dO + (int64_t)q * dm), offo, st + 8192, wave);
-    // 16 {lse, D} pairs per wave: lanes 0..7 load two each
-    if (lane < 8) lds_dma16(buffer_at(lsed_bh + q + 16 * wave), (uint32_t)(lane * 16), st + 16384 + wave * 128);
+    // per wave 16 queries: their lse log2 e (64 bytes), then their -D (64 bytes)
+    if (lane < 8) lds_dma16(buffer_at(lsd_bh + q + 16 * wave), lsd_off, st + 16384 + wave * 128);
   };
 #pragma unroll
   for (int t = 0; t < NST - 1; ++t)
@@ -706,12 +709,21 @@ __global__ __launch_bounds__(THREADS, 2) void attn_bwd_dkdv64_kernel(
     if (t + NST - 1 < ntl) issue(t + NST - 1);
     const char* qt = smem + ST * B64_STAGE;
     const char* dot = qt + 8192;
-    const float* ls = reinterpret_cast<const float*>(qt + 16384);
+    const char* ls = qt + 16384;
     const int q = (qt0 + t) * 64;
+    // rows mfma_row(4g .. 4g+3, h) of sub-tile ib: queries il .. il+3 of the tile, il = 32 ib + 8 g
+    // + 4 h; their 16-query group holds lse log2 e at +0 and -D at +64
+    auto lsd_at = [&](int ib, int g) { const int il = ib * 32 + g * 8 + h * 4; return ls + (il >> 4) * 128 + (il & 15) * 4; };
     // one 32-query sub-tile in three steps: S and dP, then P and dS, then dV and dK
     auto scores = [&](int ib, f32x16& sacc, f32x16& dpacc) {
       sacc = f32x16{};
-      dpacc = f32x16{};
+      // dP starts from -D, so that the MFMAs leave dP - D
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const f32x4 nd = *reinterpret_cast<const f32x4*>(lsd_at(ib, g) + 64);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) dpacc[4 * g + e] = nd[e];
+      }
 #pragma unroll
       for (int s = 0; s < 4; ++s) {
         Mfma<bf16>::mma(sacc, HeadTile::frag(qt, ib * 32, s, lane), kf[s]);
@@ -723,15 +735,12 @@ __global__ __launch_bounds__(THREADS, 2) void attn_bwd_dkdv64_kernel(
       float p[16], ds[16];
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
-        const int il = ib * 32 + g * 8 + h * 4;  // rows mfma_row(4g .. 4g+3, h)
-        const f32x4 a = *reinterpret_cast<const f32x4*>(ls + 2 * il);      // lse0 D0 lse1 D1
-        const f32x4 bb = *reinterpret_cast<const f32x4*>(ls + 2 * il + 4);  // lse2 D2 lse3 D3
-        const float lv[4] = {a[0], a[2], bb[0], bb[2]}, dd[4] = {a[1], a[3], bb[1], bb[3]};
+        const f32x4 lv = *reinterpret_cast<const f32x4*>(lsd_at(ib, g));
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           const int r = 4 * g + e;
           p[r] = fast_exp2(fmaf(sacc[r], c, -lv[e]));
-          ds[r] = p[r] * (dpacc[r] - dd[e]);
+          ds[r] = p[r] * dpacc[r];
         }
       }
       if (diag) {  // queries before the key: zero (a branch of its own, taken on diagonal tiles)
@@ -806,13 +815,13 @@ __global__ __launch_bounds__(THREADS, 2) void attn_bwd_dkdv64_kernel(
 // keeps a wave at about 130 registers, so three blocks (48 KB of LDS each) share a CU; two groups
 // per wave (256 queries per block) needed about 200 registers and ran two waves per SIMD, about 8 %
 // slower over the whole attention backward at the GPT-2 124M shape. Each query's D = dO . O is
-// computed here from its own rows and written with lse log2 e as the pair the dK/dV kernel
-// (launched after this one) reads.
+// computed here from its own rows and written, negated, beside lse log2 e for the dK/dV kernel
+// (launched after this one).
 constexpr int DQ64_Q = 128;  // queries per block
 
 __global__ __launch_bounds__(THREADS, 3) void attn_bwd_dq64_kernel(
     const bf16* __restrict__ qkv, const bf16* __restrict__ out, const bf16* __restrict__ dout,
-    const float* __restrict__ lse, float2* __restrict__ lsed, bf16* __restrict__ dqkv, int T_,
+    const float* __restrict__ lse, float* __restrict__ lsd, bf16* __restrict__ dqkv, int T_,
     int H) {
   constexpr int NST = 3;
   constexpr int LW = 2 * HeadTile::PER_WAVE;
@@ -855,8 +864,12 @@ __global__ __launch_bounds__(THREADS, 3) void attn_bwd_dq64_kernel(
     dsum = part + __shfl_xor(part, 32, 64);
   }
   const float lse2 = qi < T_ ? lse[(int64_t)bh * T_ + qi] * LOG2E : 0.0f;
-  // the {lse log2 e, D} pairs the dK/dV kernel streams with its query tiles
-  if (h == 0 && qi < T_) lsed[(int64_t)bh * T_ + qi] = make_float2(lse2, dsum);
+  // lse log2 e and -D, which the dK/dV kernel streams with its query tiles (two arrays of
+  // B H T floats)
+  if (h == 0 && qi < T_) {
+    lsd[(int64_t)bh * T_ + qi] = lse2;
+    lsd[((int64_t)gridDim.x + bh) * T_ + qi] = -dsum;
+  }
   f32x16 dq[2];
   dq[0] = dq[1] = f32x16{};
   const float c = LOG2E / 8.0f;
@@ -965,15 +978,14 @@ hipError_t bwd_t(int B, int T_, int H, const void* qkv, const void* out, const f
   const int rows = B * T_;
   if constexpr (sizeof(T) == 2 && HD == 64) {
     if (T_ % 64 == 0) {
-      // dQ first: it also writes the {lse log2 e, D} pairs that dK/dV read
-      float2* lsed = reinterpret_cast<float2*>(dsum);
+      // dQ first: it also writes the lse log2 e and -D values that dK/dV read
       hipLaunchKernelGGL(attn_bwd_dq64_kernel, dim3(B * H, (T_ + DQ64_Q - 1) / DQ64_Q), dim3(THREADS),
                          0, s, static_cast<const bf16*>(qkv), static_cast<const bf16*>(out),
-                         static_cast<const bf16*>(dout), lse, lsed, static_cast<bf16*>(dqkv), T_,
+                         static_cast<const bf16*>(dout), lse, dsum, static_cast<bf16*>(dqkv), T_,
                          H);
       hipLaunchKernelGGL(attn_bwd_dkdv64_kernel, dim3(B * H, (T_ + B64_KEYS - 1) / B64_KEYS),
                          dim3(THREADS), 0, s, static_cast<const bf16*>(qkv),
-                         static_cast<const bf16*>(dout), lsed, static_cast<bf16*>(dqkv), T_, H);
+                         static_cast<const bf16*>(dout), dsum, static_cast<bf16*>(dqkv), T_, H);
       return hipGetLastError();
     }
   }
