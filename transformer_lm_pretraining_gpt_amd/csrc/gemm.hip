@@ -1048,9 +1048,10 @@ hipError_t launch_persistent(int tiles, int splits, const GemmParams& p, hipStre
   return hipGetLastError();
 }
 
-// Tile configurations of the direct-to-LDS kernel, both with 64-byte slabs (32 k) and three
+// Tile configurations of the direct-to-LDS kernel, all with 64-byte slabs (32 k) and three
 // stages: 256x256 with 8 waves (wave tiles 128 x 64, two waves per SIMD, 96 KB LDS, one block per
-// CU) and 128x128 with 4 waves (48 KB, up to three blocks per CU). Two waves per SIMD let one
+// CU), 128x384 with 8 waves (wave tiles 64 x 96), 256x128 with 4 waves (wave tiles 128 x 64, 72 KB,
+// two blocks per CU) and 128x128 with 4 waves (48 KB, up to three blocks per CU). Two waves per SIMD let one
 // wave's barriers and epilogue overlap the other's MFMAs; the large tile issues the fewest loads
 // per MFMA. Chosen by measurement over the GPT-2 shapes against 256x128 tiles with two blocks
 // per CU, deeper or shallower pipelines and 128-byte slabs in two stages. Tag 1 (the LM-head
@@ -1120,6 +1121,7 @@ hipError_t launch_type(int a_kmajor, int b_kmajor, int tile, int splits, int tag
         }
         return launch_layout<T, 256, 256>(a_kmajor, b_kmajor, splits, tag, p, s);
       case TILE_256: return launch_layout<T, 256, 256>(a_kmajor, b_kmajor, splits, tag, p, s);
+      case TILE_256x128: return launch_layout<T, 256, 128>(a_kmajor, b_kmajor, splits, tag, p, s);
       default: return launch_layout<T, 128, 128>(a_kmajor, b_kmajor, splits, tag, p, s);
     }
   }
