@@ -1050,11 +1050,13 @@ hipError_t launch_persistent(int tiles, int splits, const GemmParams& p, hipStre
 
 // Tile configurations of the direct-to-LDS kernel, all with 64-byte slabs (32 k) and three
 // stages: 256x256 with 8 waves (wave tiles 128 x 64, two waves per SIMD, 96 KB LDS, one block per
-// CU), 128x384 with 8 waves (wave tiles 64 x 96), 256x128 with 4 waves (wave tiles 128 x 64, 72 KB,
-// two blocks per CU) and 128x128 with 4 waves (48 KB, up to three blocks per CU). Two waves per SIMD let one
-// wave's barriers and epilogue overlap the other's MFMAs; the large tile issues the fewest loads
-// per MFMA. Chosen by measurement over the GPT-2 shapes against 256x128 tiles with two blocks
-// per CU, deeper or shallower pipelines and 128-byte slabs in two stages. Tag 1 (the LM-head
+// CU), 128x384 with 8 waves (wave tiles 64 x 96), 256x128 with 4 waves (wave tiles 128 x 64,
+// 72 KB, two blocks per CU) and 128x128 with 4 waves (48 KB, up to three blocks per CU). Two waves
+// per SIMD let one wave's barriers and epilogue overlap the other's MFMAs; the large tile issues
+// the fewest loads per MFMA. Chosen by measurement over the GPT-2 shapes against deeper or
+// shallower pipelines and 128-byte slabs in two stages; 256x128 and 128x256 tiles lose to the
+// 8-wave tiles wherever those fill the chip, and beat 128x128 on the input-gradient products
+// that the 8-wave tiles do not fill. Tag 1 (the LM-head
 // forward, an instantiation of its own so that timings and profiles can single it out) writes
 // its output with nontemporal stores.
 template <int AK, int BKM, int BM, int BN>
