@@ -22,6 +22,7 @@ def _stored(torch, logical, kmajor_rows_are_k, dtype):
 LAYOUTS = [(1, 0), (1, 1), (0, 0), (0, 1)]
 # (6104, 2296, 192): 216 tiles of 256x256 (the 8-wave configuration), ragged in m and n;
 # (4104, 4104, 192): 289 of them, more than the chip holds at once, so blocks loop over tiles
+# (k-major A runs it as 363 tiles of 128x384, the last column of tiles partly filled);
 # (16296, 768, 192) and (10000, 1152, 128): 192 and 200 tiles of 256x256 with n a multiple of 384,
 # which k-major A runs as 256 and 237 tiles of 128x384, ragged in m
 SHAPES = [(200, 136, 72), (256, 256, 128), (1000, 520, 776), (4096, 2304, 768), (64, 768, 3072),
@@ -62,7 +63,9 @@ def _bf16_round(torch, x):
 
 
 # (shape, layout): the register-staged kernel (k not a multiple of 64), the 128x128 and 256x256
-# direct-to-LDS tiles, and the 128x384 tile with either B layout and 2 or 3 column tiles
+# direct-to-LDS tiles, the 128x384 tile with either B layout and 2 or 3 column tiles, and the
+# 256x128 tile, which (1000, 520, 768) with both operands k-major takes for the plain bf16 output
+# (4 x 5 tiles, ragged in m and n)
 EPI_CASES = [((200, 136, 72), (1, 0)), ((1000, 520, 768), (1, 1)), ((1000, 520, 768), (0, 0)),
              ((6104, 2296, 192), (1, 0)), ((16296, 768, 192), (1, 0)), ((16296, 768, 192), (1, 1)),
              ((10000, 1152, 128), (1, 1))]

@@ -474,13 +474,9 @@ gpt2_status gemm(gpt2_ctx* c, int a_kmajor, int b_kmajor, int M, int N, int K, c
   Timed t1(c, FAM_GEMM, fl);
   Timed t0(c, tag == 1 ? FAM_LMHEAD : -2, fl);
   Timed t2(c, c->in_backward ? FAM_GEMM_DX : FAM_GEMM_FWD, fl);
-  int tile = pick_tile(c->g, M, N);
-  // Input-gradient products (both operands k-major, plain output) whose 256x256 tiles would not
-  // fill the chip take 256x128 tiles at two blocks per CU instead of 128x128 ones: at GPT-2 350M
-  // and 1.5B (N = 1024 and 1600) 6-14 % faster standalone. The forward products of those shapes
-  // (fp32 residual epilogue, weights read transposed) stay on 128x128 tiles, faster there.
-  if (tile == TILE_128 && c->g.bf16 && a_kmajor && b_kmajor && epi == EPI_STORE && !colsum)
-    tile = TILE_256x128;
+  const int tile = c->g.bf16
+                       ? gemm_pick_tile_epi(M, N, a_kmajor, b_kmajor, epi, colsum != nullptr)
+                       : TILE_128;
   HIPCHK(launch_gemm(c->g.bf16, a_kmajor, b_kmajor, tile, 1, tag, p, c->stream));
   return GPT2_OK;
 }
@@ -1087,7 +1083,8 @@ gpt2_status gpt2_op_gemm_epilogue(int32_t a_kmajor, int32_t b_kmajor, int32_t m,
   p.aux = epilogue == GPT2_EPI_GELU_BWD ? d_aux : nullptr;
   p.alpha = epilogue == GPT2_EPI_STORE ? alpha : 1.0f;
   p.beta = 0.0f;
-  HIPCHK(launch_gemm(true, a_kmajor ? 1 : 0, b_kmajor ? 1 : 0, gemm_pick_tile(m, n), 1, 0, p,
+  const int tile = gemm_pick_tile_epi(m, n, a_kmajor ? 1 : 0, b_kmajor ? 1 : 0, epilogue, false);
+  HIPCHK(launch_gemm(true, a_kmajor ? 1 : 0, b_kmajor ? 1 : 0, tile, 1, 0, p,
                      static_cast<hipStream_t>(hip_stream)));
   return GPT2_OK;
 }

@@ -1149,6 +1149,17 @@ int gemm_pick_tile(int M, int N) {
   return t256 >= 192 ? TILE_256 : TILE_128;
 }
 
+int gemm_pick_tile_epi(int M, int N, int a_kmajor, int b_kmajor, int epi, bool colsum) {
+  const int t = gemm_pick_tile(M, N);
+  // Products with both operands k-major and a plain bf16 output (the input gradients) whose
+  // 256x256 tiles would not fill the chip take 256x128 tiles at two blocks per CU instead of
+  // 128x128 ones: at GPT-2 350M and 1.5B (N = 1024 and 1600) 6-14 % faster standalone. The
+  // forward products of those shapes (fp32 residual epilogue, weights read transposed) are
+  // faster on 128x128 tiles.
+  if (t == TILE_128 && a_kmajor && b_kmajor && epi == EPI_STORE && !colsum) return TILE_256x128;
+  return t;
+}
+
 hipError_t launch_gemm(bool is_bf16, int a_kmajor, int b_kmajor, int tile, int splits, int tag,
                        const GemmParams& p, hipStream_t s) {
   if (p.M <= 0 || p.N <= 0) return hipSuccess;

@@ -48,6 +48,8 @@ hipError_t launch_gemm(bool is_bf16, int a_kmajor, int b_kmajor, int tile, int s
 int gemm_k_tile(bool is_bf16);
 // Measured tile choice for a bf16 product with an M x N output.
 int gemm_pick_tile(int M, int N);
+// the tile for a bf16 product with the given layouts and epilogue (colsum: fused column sums)
+int gemm_pick_tile_epi(int M, int N, int a_kmajor, int b_kmajor, int epi, bool colsum);
 
 // Sum split-K partials: C[m, n] = alpha * sum_z part[z][m, n] + beta * C[m, n] (fixed z order).
 hipError_t launch_splitk_reduce(const float* part, int splits, int64_t split_stride, int M, int N,
